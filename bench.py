@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Benchmark of the Differential Attention V2 forward hot path on one MI355X.
+
+A step is one pass of the whole path over synthetic inputs already resident in
+HBM: one causal bf16 prefill (B=1, T=4096, Hq=64, Hkv=8, d=128) followed by one
+bf16 split-KV decode (B=64, L=8192, Hq=64, Hkv=8, d=128).  The prefill and
+decode launches are each bracketed by HIP events on the stream they run on;
+`value` is the prefill's algorithmic TFLOP/s (4*d flops per visible
+query-key-head, causal) over its mean launch time, and the decode's KV-cache
+GB/s (every K/V byte once) is reported beside it.  Rank 0 prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "DiffAttn-V2 fwd: prefill TFLOP/s & decode KV GB/s, % of MI355X peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _kernel_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "differential_attention_v2_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kind: str, launches_per_record: int = 1):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != _kernel_hash(rec["sources"]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s: float) -> dict:
+    """The fp64 oracle on a bounded sample of the prefill workload: whole pairs, all 4096 rows."""
+    import numpy as np
+    import oracle
+    from differential_attention_v2_amd import workloads as W
+    try:
+        import threadpoolctl
+        threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas")
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    w = W.CONFIGS[2]
+    inp = W.make_prefill(w)
+    q, k, v = (W.to_f64(inp[n], "bf16") for n in ("q", "k", "v"))
+    G = w.G
+    done, t0 = 0, time.perf_counter()
+    while done < w.P and time.perf_counter() - t0 < budget_s:
+        p = done
+        g = p // G
+        oracle.diffattn_prefill(q[:, :, 2 * p:2 * p + 2], k[:, :, g:g + 1], v[:, :, g:g + 1],
+                                inp["lam"][:, :, p:p + 1])
+        done += 1
+    dt = time.perf_counter() - t0
+    flops = w.prefill_flops() * done / w.P
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads or 1), "kind": "oracle",
+            "sample": f"c2 prefill, {done} of {w.P} pairs x all {w.T} rows, fp64 numpy (OpenBLAS), {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one half of the step (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU sharding or collectives)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from differential_attention_v2_amd import binding as bd
+    from differential_attention_v2_amd import workloads as W
+
+    if not os.path.exists(bd.LIB_PATH):
+        from differential_attention_v2_amd import build_lib
+        build_lib.build()
+    dev = torch.device("cuda:0")
+
+    def dev_bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wp, wd = W.CONFIGS[2], W.CONFIGS[4]
+    do_p = args.only in (None, "prefill")
+    do_d = args.only in (None, "decode")
+    if do_p:
+        ip = W.make_prefill(wp)
+        pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
+        plam = torch.from_numpy(ip["lam"]).to(dev)
+        pout = torch.empty((wp.B, wp.T, wp.P, wp.d), dtype=torch.bfloat16, device=dev)
+        del ip
+    if do_d:
+        idc = W.make_decode(wd)
+        dq, dk, dv = dev_bf16(idc["q"]), dev_bf16(idc["k"]), dev_bf16(idc["v"])
+        dlam = torch.from_numpy(idc["lam"]).to(dev)
+        dout = torch.empty((wd.B, wd.P, wd.d), dtype=torch.bfloat16, device=dev)
+        dws = bd.decode_workspace(wd.B, wd.T, wd.Hq, wd.Hkv, wd.d, 0, dev)
+        del idc
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if do_p:
+            if evs: evs[0].record(stream)
+            bd.prefill(pq, pk, pv, plam, out=pout)
+            if evs: evs[1].record(stream)
+        if do_d:
+            if evs: evs[2].record(stream)
+            bd.decode(dq, dk, dv, dlam, workspace=dws, out=dout)
+            if evs: evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if do_p else None
+    ms_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) if do_d else None
+
+    src_p = ["prefill_bf16.hip", "dev_common.h"]
+    src_d = ["decode_bf16.hip", "dev_common.h"]
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms_total / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded normals; no dataset)"}
+    if do_p:
+        tflops = wp.prefill_flops() / (ms_pre * 1e-3) / 1e12
+        res.update(value=tflops, unit="TFLOP/s")
+        res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tflops / PEAK_BF16_TFLOPS, "traffic": _traffic("prefill"),
+                           "kernel": "prefill_kernel<128>", "ms_per_launch": ms_pre,
+                           "algorithmic_flops_per_launch": wp.prefill_flops()}
+    if do_d:
+        gbs = wd.decode_kv_bytes() / (ms_dec * 1e-3) / 1e9
+        res["decode"] = {"value": gbs, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "ms_per_launch": ms_dec,
+                         "workload": f"{wd.name}: B={wd.B} L={wd.T} Hq={wd.Hq} Hkv={wd.Hkv} d={wd.d} bf16",
+                         "splits": bd.diffattn_decode_num_splits(wd.B, wd.T, wd.Hq, wd.Hkv, wd.d)}
+        res["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": gbs / PEAK_HBM_GBS, "traffic": _traffic("decode"),
+                                  "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                                  "algorithmic_bytes_per_launch": wd.decode_kv_bytes()}
+        if not do_p:
+            res.update(value=gbs, unit="GB/s")
+    res["config"] = {"workload": (f"{wp.name}: B={wp.B} T={wp.T} Hq={wp.Hq} Hkv={wp.Hkv} d={wp.d} causal bf16"
+                                  if do_p else None),
+                     "decode_workload": wd.name if do_d else None,
+                     "global_batch": wp.B, "seq_len": wp.T, "parallelism": "none (1 GPU)"}
+    if not args.no_cpu_baseline and do_p:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+             "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "decode", "roofline_decode",
+             "cpu_baseline"]
+    print(json.dumps({k: res[k] for k in order if k in res}), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,202 @@
+"""Thin ctypes binding over libdiffattn (argument marshalling only).
+
+The raw functions carry the C names and arguments one to one.  ``prefill``,
+``decode`` and ``v1_lambda`` are conveniences over torch tensors: they check
+device, dtype, shape and contiguity, allocate outputs/workspace with torch (torch
+is only the memory and stream provider) and pass raw pointers plus the current
+HIP stream.  Every step of the computation runs in the library's kernels; if the
+library is missing this module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdiffattn.so")
+
+DIFFATTN_OK = 0
+DIFFATTN_ERR_INVALID_ARG = 1
+DIFFATTN_ERR_UNSUPPORTED = 2
+DIFFATTN_ERR_WORKSPACE = 3
+DIFFATTN_ERR_HIP = 4
+DIFFATTN_BF16 = 0
+DIFFATTN_FP32 = 1
+DIFFATTN_FLAG_V1_RMSNORM = 0x1
+
+_c_int, _c_uint, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_uint, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGNATURES = {
+    "diffattn_prefill_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                      _c_int, _c_uint, _c_float, _vp]),
+    "diffattn_decode_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, _c_uint, _c_float, _c_int, _vp, _c_size, _vp]),
+    "diffattn_decode_num_splits": (_c_int, [_c_int] * 5),
+    "diffattn_decode_workspace_bytes": (_c_size, [_c_int] * 6),
+    "diffattn_v1_lambda": (_c_int, [_vp, _vp, _vp, _vp, _c_float, _vp, _c_int, _c_int, _c_int, _vp]),
+    "diffattn_status_string": (ctypes.c_char_p, [_c_int]),
+    "diffattn_version": (_c_int, []),
+}
+
+_lib = None
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: libdiffattn status {status} ({status_string(status)})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdiffattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m differential_attention_v2_amd.build_lib` "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+# ---- raw C entry points, same names and arguments as include/diffattn.h ----
+def diffattn_prefill_fwd(q, k, v, lam, out, B, T, Hq, Hkv, d, causal, dtype, flags, rms_eps, stream):
+    return load_library().diffattn_prefill_fwd(q, k, v, lam, out, B, T, Hq, Hkv, d, causal, dtype, flags,
+                                               rms_eps, stream)
+
+
+def diffattn_decode_fwd(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, flags, rms_eps, num_splits,
+                        workspace, workspace_bytes, stream):
+    return load_library().diffattn_decode_fwd(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, flags,
+                                              rms_eps, num_splits, workspace, workspace_bytes, stream)
+
+
+def diffattn_decode_num_splits(B, L, Hq, Hkv, d):
+    return load_library().diffattn_decode_num_splits(B, L, Hq, Hkv, d)
+
+
+def diffattn_decode_workspace_bytes(B, L, Hq, Hkv, d, num_splits=0):
+    return load_library().diffattn_decode_workspace_bytes(B, L, Hq, Hkv, d, num_splits)
+
+
+def diffattn_v1_lambda(lq1, lk1, lq2, lk2, lambda_init, lambda_out, P, d_lambda, rows, stream):
+    return load_library().diffattn_v1_lambda(lq1, lk1, lq2, lk2, lambda_init, lambda_out, P, d_lambda, rows,
+                                             stream)
+
+
+def diffattn_status_string(status):
+    return load_library().diffattn_status_string(status)
+
+
+def diffattn_version():
+    return load_library().diffattn_version()
+
+
+def status_string(status: int) -> str:
+    return diffattn_status_string(status).decode()
+
+
+# ---- torch conveniences ----
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DIFFATTN_BF16
+    if t.dtype == torch.float32:
+        return DIFFATTN_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32")
+
+
+def _check(t, name, shape, dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def prefill(q, k, v, lam, causal: bool = True, v1_rmsnorm: bool = False, eps: float = 1e-5, out=None,
+            stream=None):
+    """out [B, T, P, d] = DiffAttn V2 prefill of q [B,T,Hq,d], k/v [B,T,Hkv,d], lam [B,T,P] (fp32)."""
+    torch = _torch()
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    _check(q, "q", (B, T, Hq, d), q.dtype)
+    _check(k, "k", (B, T, Hkv, d), q.dtype)
+    _check(v, "v", (B, T, Hkv, d), q.dtype)
+    _check(lam, "lam", (B, T, Hq // 2), torch.float32)
+    if out is None:
+        out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device)
+    _check(out, "out", (B, T, Hq // 2, d), q.dtype)
+    st = diffattn_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(), out.data_ptr(), B, T, Hq,
+                              Hkv, d, int(bool(causal)), _dtype_code(q),
+                              DIFFATTN_FLAG_V1_RMSNORM if v1_rmsnorm else 0, float(eps), _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_prefill_fwd")
+    return out
+
+
+def decode_workspace(B, L, Hq, Hkv, d, num_splits: int = 0, device="cuda"):
+    torch = _torch()
+    n = diffattn_decode_workspace_bytes(B, L, Hq, Hkv, d, num_splits)
+    if n == 0:
+        raise ValueError("invalid decode sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode(q, k_cache, v_cache, lam, v1_rmsnorm: bool = False, eps: float = 1e-5, num_splits: int = 0,
+           workspace=None, out=None, stream=None):
+    """out [B, P, d] = DiffAttn V2 decode of q [B,Hq,d] over caches [B,L,Hkv,d] with lam [B,P] (fp32)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(q, "q", (B, Hq, d), q.dtype)
+    _check(k_cache, "k_cache", (B, L, Hkv, d), q.dtype)
+    _check(v_cache, "v_cache", (B, L, Hkv, d), q.dtype)
+    _check(lam, "lam", (B, Hq // 2), torch.float32)
+    if out is None:
+        out = torch.empty((B, Hq // 2, d), dtype=q.dtype, device=q.device)
+    _check(out, "out", (B, Hq // 2, d), q.dtype)
+    if workspace is None and q.dtype == torch.bfloat16:
+        workspace = decode_workspace(B, L, Hq, Hkv, d, num_splits, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = diffattn_decode_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lam.data_ptr(), out.data_ptr(),
+                             B, L, Hq, Hkv, d, _dtype_code(q), DIFFATTN_FLAG_V1_RMSNORM if v1_rmsnorm else 0,
+                             float(eps), int(num_splits), ws_ptr, ws_bytes, _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_decode_fwd")
+    return out
+
+
+def v1_lambda(lq1, lk1, lq2, lk2, lambda_init: float, rows: int, out=None, stream=None):
+    """lambda [rows, P] = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init per pair, broadcast over rows."""
+    torch = _torch()
+    P, dl = lq1.shape
+    for name, t in (("lq1", lq1), ("lk1", lk1), ("lq2", lq2), ("lk2", lk2)):
+        _check(t, name, (P, dl), torch.float32)
+    if out is None:
+        out = torch.empty((rows, P), dtype=torch.float32, device=lq1.device)
+    _check(out, "out", (rows, P), torch.float32)
+    st = diffattn_v1_lambda(lq1.data_ptr(), lk1.data_ptr(), lq2.data_ptr(), lk2.data_ptr(), float(lambda_init),
+                            out.data_ptr(), P, dl, rows, _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_v1_lambda")
+    return out

@@ -1,0 +1,150 @@
+// C-ABI entry points of libdiffattn: argument validation, split planning and
+// dispatch to the gfx950 kernels.  Every check runs on the host before anything
+// is enqueued, so an invalid call writes nothing and touches no device.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <cmath>
+
+#include "diffattn.h"
+#include "internal.h"
+
+using namespace diffattn;
+
+namespace {
+
+constexpr int kVersion = 100;                    // 0.1.0
+constexpr long long kMaxElems = 1LL << 40;       // per tensor
+constexpr long long kMaxGrid = (1LL << 31) - 1;  // workgroups per launch
+constexpr int kDecodeTargetWaves = 4096;         // ~16 waves per CU on 256 CUs
+
+bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_heads(int Hq, int Hkv, int d) {
+  if (Hkv < 1 || Hq < 2 || Hq % (2 * Hkv) != 0) return DIFFATTN_ERR_INVALID_ARG;
+  if (d <= 0) return DIFFATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return DIFFATTN_ERR_UNSUPPORTED;
+  if (Hq / (2 * Hkv) > 8) return DIFFATTN_ERR_UNSUPPORTED;
+  return DIFFATTN_OK;
+}
+
+int check_mode(int dtype, unsigned flags, float eps) {
+  if (dtype != DIFFATTN_BF16 && dtype != DIFFATTN_FP32) return DIFFATTN_ERR_INVALID_ARG;
+  if (flags & ~DIFFATTN_FLAG_V1_RMSNORM) return DIFFATTN_ERR_INVALID_ARG;
+  if ((flags & DIFFATTN_FLAG_V1_RMSNORM) && !(std::isfinite(eps) && eps > 0.f)) return DIFFATTN_ERR_INVALID_ARG;
+  return DIFFATTN_OK;
+}
+
+bool fits(long long a, long long b, long long c, long long d) {
+  // a*b*c*d <= kMaxElems without overflowing (all >= 1)
+  long long x = a;
+  for (long long y : {b, c, d}) {
+    if (x > kMaxElems / y) return false;
+    x *= y;
+  }
+  return true;
+}
+
+// Key-range split of a decode problem: S ranges of `chunk` keys (a multiple of 32).
+bool decode_plan(int B, int L, int Hkv, int num_splits, int* S, int* chunk) {
+  if (B < 1 || L < 1 || Hkv < 1 || num_splits < 0) return false;
+  const long long units = (long long)B * Hkv;
+  const long long nblk = (L + 31) / 32;
+  long long want = num_splits > 0 ? num_splits : (kDecodeTargetWaves + units - 1) / units;
+  if (want > nblk) want = nblk;
+  if (want < 1) want = 1;
+  const long long per = (nblk + want - 1) / want;
+  *chunk = (int)(per * 32);
+  *S = (int)((L + *chunk - 1) / *chunk);
+  return units * *S <= kMaxGrid;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_prefill_fwd(const void* q, const void* k, const void* v, const float* lambda, void* out, int B, int T,
+                         int Hq, int Hkv, int d, int causal, int dtype, unsigned flags, float rms_eps, void* stream) {
+  if (B < 1 || T < 1) return DIFFATTN_ERR_INVALID_ARG;
+  int st = check_heads(Hq, Hkv, d);
+  if (st) return st;
+  st = check_mode(dtype, flags, rms_eps);
+  if (st) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lambda, 4))
+    return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(B, T, Hq, d) || (long long)B * T * (Hq / 2) > kMaxGrid) return DIFFATTN_ERR_INVALID_ARG;
+
+  PrefillProblem p{q, k, v, lambda, out, B, T, Hq, Hkv, d, causal ? 1 : 0,
+                   (flags & DIFFATTN_FLAG_V1_RMSNORM) ? 1 : 0, rms_eps};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == DIFFATTN_FP32) return hip_status(launch_rows_f32(p, T, T, s));
+  return hip_status(launch_prefill_bf16(p, s));
+}
+
+int diffattn_decode_num_splits(int B, int L, int Hq, int Hkv, int d) {
+  if (check_heads(Hq, Hkv, d) != DIFFATTN_OK) return 0;
+  int S, chunk;
+  return decode_plan(B, L, Hkv, 0, &S, &chunk) ? S : 0;
+}
+
+size_t diffattn_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d, int num_splits) {
+  if (check_heads(Hq, Hkv, d) != DIFFATTN_OK) return 0;
+  int S, chunk;
+  if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return 0;
+  return (size_t)B * Hq * S * decode_record_floats(d) * sizeof(float);
+}
+
+int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, const float* lambda, void* out,
+                        int B, int L, int Hq, int Hkv, int d, int dtype, unsigned flags, float rms_eps,
+                        int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || L < 1 || num_splits < 0) return DIFFATTN_ERR_INVALID_ARG;
+  int st = check_heads(Hq, Hkv, d);
+  if (st) return st;
+  st = check_mode(dtype, flags, rms_eps);
+  if (st) return st;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(lambda, 4))
+    return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(B, L, Hkv, d) || !fits(B, Hq, d, 1)) return DIFFATTN_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int v1 = (flags & DIFFATTN_FLAG_V1_RMSNORM) ? 1 : 0;
+
+  if (dtype == DIFFATTN_FP32) {
+    // one query row at position L-1: causal with Tq = 1 sees every cache row
+    PrefillProblem p{q, k_cache, v_cache, lambda, out, B, L, Hq, Hkv, d, 1, v1, rms_eps};
+    return hip_status(launch_rows_f32(p, 1, L, s));
+  }
+  int S, chunk;
+  if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return DIFFATTN_ERR_INVALID_ARG;
+  const size_t need = (size_t)B * Hq * S * decode_record_floats(d) * sizeof(float);
+  if (!aligned(workspace, 16) || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+  DecodeProblem p{q, k_cache, v_cache, lambda, out, static_cast<float*>(workspace), B, L, Hq, Hkv, d, S, chunk,
+                  v1, rms_eps};
+  return hip_status(launch_decode_bf16(p, s));
+}
+
+int diffattn_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2, float lambda_init,
+                       float* lambda_out, int P, int d_lambda, int rows, void* stream) {
+  if (P < 1 || d_lambda < 1 || rows < 1 || !std::isfinite(lambda_init)) return DIFFATTN_ERR_INVALID_ARG;
+  if (!aligned(lq1, 4) || !aligned(lk1, 4) || !aligned(lq2, 4) || !aligned(lk2, 4) || !aligned(lambda_out, 4))
+    return DIFFATTN_ERR_INVALID_ARG;
+  if ((long long)rows * P > kMaxGrid * 256LL || !fits(P, d_lambda, 1, 1)) return DIFFATTN_ERR_INVALID_ARG;
+  return hip_status(launch_v1_lambda(lq1, lk1, lq2, lk2, lambda_init, lambda_out, P, d_lambda, rows,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+const char* diffattn_status_string(int status) {
+  switch (status) {
+    case DIFFATTN_OK: return "ok";
+    case DIFFATTN_ERR_INVALID_ARG: return "invalid argument";
+    case DIFFATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DIFFATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case DIFFATTN_ERR_HIP: return "HIP runtime or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int diffattn_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,253 @@
+// Split-KV decode for Differential Attention V2, bf16 cache / fp32 accumulate, gfx950.
+//
+// One new query token per sequence attends to a contiguous cache [B, L, Hkv, d]
+// that already holds it.  Decode is bound by HBM bandwidth, and the V2 layout
+// lets one pass over the cache serve both heads of every pair in a KV-head group
+// (dailytechsnack.ch article, section "Gemeinsamer KV-Cache statt Spezialkernel":
+// the KV cache does not grow and decoding runs at standard-transformer speed;
+// differential-attention lesson, section "V1 vs V2": V2 loads the KV cache once
+// per step and raises decode arithmetic intensity).
+//
+// Split kernel: one wave per (b, KV head g, key range s).  It streams its key
+// range once, 32 keys per step, with 16-byte loads (16 lanes cover one 256-byte
+// cache row), and computes the scores of the group's 2G query heads at once on
+// v_mfma_f32_16x16x32_bf16 (A = 16 cache keys straight from the loads, B = the
+// 2G query heads, padded to 16 columns).  P^T stays in registers as the B operand
+// of O^T += V^T P^T; the V^T operand is read from a row-major copy of the V rows
+// in LDS with the transposing LDS read.  Each wave writes, per query head, its
+// partial softmax state (running max m in the log2 domain, denominator l and the
+// unnormalised accumulator) to the workspace.
+//
+// Combine kernel: one workgroup per (b, pair).  For both heads of the pair it
+// merges the partial states (M = max_s m_s, weights 2^(m_s - M)), normalises,
+// forms o_1 - lambda * o_2 (optional V1 RMSNorm) and writes bf16.
+#include "dev_common.h"
+#include "internal.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int KSTEP = 32;   // keys per step
+
+struct Args {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const float* lam;
+  bf16* out;
+  float* ws;
+  int B, L, Hq, Hkv, G, P;
+  int S, chunk;
+  int v1;
+  float eps, scale_log2;
+};
+
+// V rows in LDS: row-major [key][d], 16-byte chunks XOR-permuted per row so the
+// transposing reads of 8 rows x 2 chunks hit distinct banks.
+template <int D>
+__device__ __forceinline__ int v_phys(int row, int col) {
+  constexpr int NCH = D / 8;
+  const int sw = (NCH >= 16) ? ((row & 7) << 1) : ((row & 3) << 1);
+  return row * D + ((((col >> 3) ^ sw)) << 3) + (col & 7);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
+  constexpr int KS = D / 32;                 // QK^T k-steps (k = 32 per MFMA)
+  constexpr int DB = D / 16;                 // PV d-blocks (16 rows per MFMA)
+  constexpr int NCH = D / 8;                 // 16-byte chunks per cache row
+  constexpr int VLOADS = KSTEP * NCH / 64;   // V chunks per lane per step
+  __shared__ __attribute__((aligned(16))) bf16 vs[KSTEP * D];
+
+  const int lane = threadIdx.x;
+  const int n = lane & 15;     // query column = head within the group
+  const int grp = lane >> 4;   // 16-lane group
+  const int nq = 2 * a.G;
+
+  const int s = blockIdx.x % a.S;
+  const int bg = blockIdx.x / a.S;
+  const int g = bg % a.Hkv;
+  const int b = bg / a.Hkv;
+  const int k0 = s * a.chunk;
+  const int k1 = min(a.L, k0 + a.chunk);
+
+  // Q^T operand: column n = head g*2G + n, d = 32*ks + 8*grp + 0..7
+  bf16x8 qr[KS];
+  {
+    const bool ok = n < nq;
+    const bf16* src = a.q + ((size_t)b * a.Hq + g * nq + (ok ? n : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 x = ok ? ldg16(src + 32 * ks) : u32x4{0, 0, 0, 0};
+      qr[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  const size_t row = (size_t)a.Hkv * D;
+  const bf16* kb0 = a.k + ((size_t)b * a.L * a.Hkv + g) * D;
+  const bf16* vb0 = a.v + ((size_t)b * a.L * a.Hkv + g) * D;
+  const float c = a.scale_log2;
+
+  f32x4 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x4{};
+  float m = -INFINITY, l = 0.f;
+
+  for (int kk = k0; kk < k1; kk += KSTEP) {
+    // ---- issue all loads of this step: K as MFMA A operands, V rows for LDS
+    u32x4 ka[2][KS];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int key = kk + 16 * h + n;
+      const bool ok = key < k1;
+      const bf16* src = kb0 + (size_t)(ok ? key : k0) * row + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[h][ks] = ok ? ldg16(src + 32 * ks) : u32x4{0, 0, 0, 0};
+    }
+    u32x4 vr[VLOADS];
+#pragma unroll
+    for (int j = 0; j < VLOADS; ++j) {
+      const int cid = lane + 64 * j;
+      const int r = cid / NCH, ch = cid % NCH;
+      const int key = kk + r;
+      vr[j] = key < k1 ? ldg16(vb0 + (size_t)key * row + 8 * ch) : u32x4{0, 0, 0, 0};
+    }
+    // ---- S^T = K Q^T: lane -> query n, keys kk + 16*h + 4*grp + i
+    f32x4 s0 = f32x4{}, s1 = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = mfma16(__builtin_bit_cast(bf16x8, ka[0][ks]), qr[ks], s0);
+      s1 = mfma16(__builtin_bit_cast(bf16x8, ka[1][ks]), qr[ks], s1);
+    }
+    if (kk + KSTEP > k1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (kk + 4 * grp + i >= k1) s0[i] = -INFINITY;
+        if (kk + 16 + 4 * grp + i >= k1) s1[i] = -INFINITY;
+      }
+    }
+    // ---- online softmax over this step's 32 keys
+    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx * c);
+    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+    const float mb = (mn == -INFINITY) ? 0.f : mn;
+    m = mn;
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb[i] = (bf16)fast_exp2(__builtin_fmaf(s0[i], c, -mb));
+      pb[4 + i] = (bf16)fast_exp2(__builtin_fmaf(s1[i], c, -mb));
+    }
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) l = dot2_ones(bf16x2{pb[j], pb[j + 1]}, l);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+
+    // ---- V rows to LDS, then O^T += V^T P^T
+#pragma unroll
+    for (int j = 0; j < VLOADS; ++j) {
+      const int cid = lane + 64 * j;
+      const int r = cid / NCH, ch = cid % NCH;
+      sts16(&vs[v_phys<D>(r, 8 * ch)], vr[j]);
+    }
+    __syncthreads();
+    {
+      const int r0 = 4 * grp + (n >> 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int col = 16 * db + 4 * (n & 3);
+        const bf16x4 va = lds_read_tr4(&vs[v_phys<D>(r0, col)]);
+        const bf16x4 vb = lds_read_tr4(&vs[v_phys<D>(r0 + 16, col)]);
+        o[db] = mfma16(concat(va, vb), pb, o[db]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- partial state per query head: acc[d] (unnormalised), m, l
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (n >= nq) return;
+  const int rec = D + 4;
+  float* w = a.ws + (((size_t)b * a.Hq + g * nq + n) * a.S + s) * rec;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(w + 16 * db + 4 * grp) = o[db];
+  if (grp == 0) {
+    w[D] = m;
+    w[D + 1] = l;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(Args a) {
+  __shared__ float red[D / 64];
+  const int bp = blockIdx.x;
+  const int b = bp / a.P, p = bp % a.P;
+  const int d = threadIdx.x;
+  const int rec = D + 4;
+  float o[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float* base = a.ws + ((size_t)b * a.Hq + 2 * p + h) * a.S * rec;
+    float M = -INFINITY;
+    for (int s = 0; s < a.S; ++s) M = fmaxf(M, base[s * rec + D]);
+    float acc = 0.f, den = 0.f;
+    for (int s = 0; s < a.S; ++s) {
+      const float ms = base[s * rec + D];
+      const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+      acc += wgt * base[s * rec + d];
+      den += wgt * base[s * rec + D + 1];
+    }
+    o[h] = acc / den;
+  }
+  float x = o[0] - a.lam[(size_t)b * a.P + p] * o[1];
+  if (a.v1) {
+    float ss = x * x;
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((d & 63) == 0) red[d >> 6] = ss;
+    __syncthreads();
+    ss = 0.f;
+    for (int i = 0; i < D / 64; ++i) ss += red[i];
+    x *= 1.0f / sqrtf(ss / (float)D + a.eps);
+  }
+  a.out[((size_t)b * a.P + p) * D + d] = (bf16)x;
+}
+
+template <int D>
+hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
+  Args a;
+  a.q = static_cast<const bf16*>(pr.q);
+  a.k = static_cast<const bf16*>(pr.k);
+  a.v = static_cast<const bf16*>(pr.v);
+  a.lam = pr.lam;
+  a.out = static_cast<bf16*>(pr.out);
+  a.ws = pr.ws;
+  a.B = pr.B;
+  a.L = pr.L;
+  a.Hq = pr.Hq;
+  a.Hkv = pr.Hkv;
+  a.G = pr.Hq / (2 * pr.Hkv);
+  a.P = pr.Hq / 2;
+  a.S = pr.splits;
+  a.chunk = pr.chunk;
+  a.v1 = pr.v1_rmsnorm ? 1 : 0;
+  a.eps = pr.eps;
+  a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  const long long blocks = (long long)a.B * a.Hkv * a.S;
+  hipLaunchKernelGGL(decode_split_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.B * a.P)), dim3(D), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeProblem& p, hipStream_t s) {
+  return p.d == 128 ? launch<128>(p, s) : launch<64>(p, s);
+}
+
+}  // namespace diffattn

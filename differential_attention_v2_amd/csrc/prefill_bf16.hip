@@ -1,0 +1,358 @@
+// Tiled prefill kernel for Differential Attention V2, bf16 in / fp32 accumulate, gfx950.
+//
+// What it computes (sources: the Differential Transformer V2 web pages):
+//   out[b,i,p,:] = softmax(q_{2p} K^T/sqrt(d)) V - lambda[b,i,p] * softmax(q_{2p+1} K^T/sqrt(d)) V
+// over the keys j <= i (causal) or all keys, where both query heads of pair p
+// read the same K/V head g = p / G -- differential-attention lesson "差异性注意力
+// (V2)", section "差异性概念" (DiffAttn equation); dailytechsnack.ch article,
+// section "Gemeinsamer KV-Cache statt Spezialkernel" (adjacent query heads of one
+// GQA group share K/V and the head dim); attention-variants lesson, "步骤1"
+// (causal mask).
+//
+// Work decomposition.  A workgroup of 4 waves owns one (batch b, KV head g)
+// and a block of query tokens.  Each wave owns one differential pair p of that
+// group and 32 query tokens, i.e. 64 query rows (32 tokens x the pair's two
+// heads), so the lambda-subtract happens in registers.  Every K/V tile of 64
+// keys is copied from HBM/L2 into LDS once per workgroup and read by all waves:
+// with G = 4 pairs per KV head, one staged byte serves all 8 query heads.
+//
+// Per 32-key half-tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// (A = K from LDS, B = Q^T held in registers), so each lane holds the scores of
+// one query against 16 keys; the matching lane l^32 holds the other 16.  Two
+// online-softmax states (one per head of the pair) are kept per query; the
+// running maximum is raised lazily (only when a row's tile maximum exceeds it by
+// more than 2^8), which leaves the result unchanged because numerator and
+// denominator share the stale maximum.  P = exp2(S*log2(e)/sqrt(d) - m) is
+// rounded to bf16 and fed straight from registers as the B operand of
+// O^T += V^T P^T; the V^T operand comes from the row-major V tile via the
+// transposing LDS read.  The epilogue normalises both heads, subtracts
+// lambda * head2 from head1 (optional V1 RMSNorm) and stores bf16.
+#include "dev_common.h"
+#include "internal.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int BN = 64;           // keys per LDS tile
+constexpr int QB = 32;           // query tokens per wave
+constexpr int WAVES = 4;
+constexpr int THREADS = 64 * WAVES;
+constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold (log2 domain)
+
+struct Args {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const float* lam;
+  bf16* out;
+  int B, T, Hq, Hkv, G, P;
+  int causal, v1;
+  float eps, scale_log2;
+  int ppw;     // pairs per workgroup
+  int nsub;    // 32-token sub-blocks per workgroup
+  int chunks;  // workgroups needed to cover the G pairs of one KV head
+  int ntb;     // token blocks
+  int units;   // B * Hkv * chunks
+};
+
+// LDS layouts: tiles are row-major [key][d] without padding; 16-byte chunks of a
+// row are XOR-permuted so that the MFMA operand reads hit distinct banks.
+template <int D>
+__device__ __forceinline__ int k_phys(int row, int col) {   // col in elements
+  constexpr int NCH = D / 8;
+  return row * D + ((((col >> 3) ^ (row & (NCH - 1)))) << 3) + (col & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_phys(int row, int col) {
+  constexpr int NCH = D / 8;
+  const int sw = (NCH >= 16) ? ((row & 3) << 2) : ((row & 1) << 2);
+  return row * D + ((((col >> 3) ^ sw)) << 3) + (col & 7);
+}
+
+template <int D>
+__global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
+  constexpr int NCH = D / 8;               // 16-byte chunks per row
+  constexpr int KSTEPS = D / 16;           // QK^T k-steps
+  constexpr int DBLK = D / 32;             // PV output d-blocks
+  constexpr int LOADS = BN * NCH / THREADS;  // 16-byte chunks per thread per tile (K or V)
+  static_assert(LOADS >= 1 && (BN * NCH) % THREADS == 0, "tile/thread mismatch");
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * D];   // [buffer][K|V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool lo = lane < 32;
+  const int l32 = lane & 31;
+
+  // ---- workgroup -> (token block, b, g, pair chunk).  Token blocks run longest
+  // first (causal work grows with the block index); when the (b, g, chunk) units
+  // divide evenly over the 8 XCDs, all blocks of one unit land on one XCD so
+  // its K/V stays in that XCD's L2.
+  int tb, u;
+  {
+    const int idx = blockIdx.x;
+    if ((a.units & 7) == 0) {
+      const int upx = a.units >> 3;
+      const int slot = idx >> 3;
+      tb = a.ntb - 1 - slot / upx;
+      u = (idx & 7) + 8 * (slot % upx);
+    } else {
+      tb = a.ntb - 1 - idx / a.units;
+      u = idx % a.units;
+    }
+  }
+  const int chunk = u % a.chunks;
+  const int bg = u / a.chunks;
+  const int g = bg % a.Hkv;
+  const int b = bg / a.Hkv;
+  const int tokens_wg = QB * a.nsub;
+  const int tok0 = tb * tokens_wg;
+  const int sub = wave / a.ppw;
+  const int pig = chunk * a.ppw + (wave % a.ppw);
+  const bool active = sub < a.nsub && pig < a.G;
+  const int p = g * a.G + pig;
+  const int i0 = tok0 + sub * QB;          // first query token of this wave
+  const int T = a.T;
+
+  const int kv_end = a.causal ? min(T, tok0 + tokens_wg) : T;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  const size_t kv_row = (size_t)a.Hkv * D;                       // elements between keys
+  const bf16* kbase = a.k + ((size_t)b * T * a.Hkv + g) * D;
+  const bf16* vbase = a.v + ((size_t)b * T * a.Hkv + g) * D;
+
+  // ---- Q^T operand in registers: lane -> query token i0 + l32, d = 16*s + 8*(lane/32) + 0..7
+  bf16x8 qreg[2][KSTEPS];
+  {
+    const int qi = i0 + l32;
+    const bool ok = active && qi < T;
+    for (int h = 0; h < 2; ++h) {
+      const bf16* src = a.q + (((size_t)b * T + (ok ? qi : 0)) * a.Hq + 2 * p + h) * D + 8 * (lane >> 5);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        u32x4 x = ok ? ldg16(src + 16 * s) : u32x4{0, 0, 0, 0};
+        qreg[h][s] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+  }
+
+  f32x16 o0[DBLK], o1[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) {
+    o0[i] = f32x16{};
+    o1[i] = f32x16{};
+  }
+  float m0 = -INFINITY, m1 = -INFINITY;   // running maxima (log2 domain), uniform over l, l^32
+  float l0 = 0.f, l1 = 0.f;               // this lane's share of the softmax denominators
+  const float c = a.scale_log2;
+
+  u32x4 kr[LOADS], vr[LOADS];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int cid = tid + j * THREADS;
+      const int r = cid / NCH, ch = cid % NCH;
+      const int key = t * BN + r;
+      if (key < T) {
+        kr[j] = ldg16(kbase + key * kv_row + 8 * ch);
+        vr[j] = ldg16(vbase + key * kv_row + 8 * ch);
+      } else {
+        kr[j] = u32x4{0, 0, 0, 0};
+        vr[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int cid = tid + j * THREADS;
+      const int r = cid / NCH, ch = cid % NCH;
+      sts16(&smem[buf][0][k_phys<D>(r, 8 * ch)], kr[j]);
+      sts16(&smem[buf][1][v_phys<D>(r, 8 * ch)], vr[j]);
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1);
+
+    if (active) {
+      const bf16* Kt = smem[buf][0];
+      const bf16* Vt = smem[buf][1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kbase_tok = t * BN + kb * 32;
+        if (kbase_tok >= T) break;
+        if (a.causal && kbase_tok > i0 + QB - 1) break;
+
+        // ---- S^T = K Q^T for both heads (keys x queries)
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+        {
+          const int r = kb * 32 + l32;
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kt[k_phys<D>(r, 16 * s + 8 * (lane >> 5))]);
+            s0 = mfma32(ka, qreg[0][s], s0);
+            s1 = mfma32(ka, qreg[1][s], s1);
+          }
+        }
+        // ---- masking: causal diagonal and sequence tail
+        if ((a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T) {
+          const int qi = i0 + l32;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            const bool vis = key < T && (!a.causal || key <= qi);
+            if (!vis) {
+              s0[i] = -INFINITY;
+              s1[i] = -INFINITY;
+            }
+          }
+        }
+        // ---- online softmax, lazily rescaled
+        float mx0 = s0[0], mx1 = s1[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+          mx0 = fmaxf(mx0, s0[i]);
+          mx1 = fmaxf(mx1, s1[i]);
+        }
+        mx0 = fmaxf(mx0, partner32(mx0, lo)) * c;
+        mx1 = fmaxf(mx1, partner32(mx1, lo)) * c;
+        const bool grow = (mx0 > m0 + RESCALE_LOG2) || (mx1 > m1 + RESCALE_LOG2);
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float n0 = fmaxf(m0, mx0), n1 = fmaxf(m1, mx1);
+          const float a0 = (n0 == -INFINITY) ? 1.f : fast_exp2(m0 - n0);
+          const float a1 = (n1 == -INFINITY) ? 1.f : fast_exp2(m1 - n1);
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) {
+            o0[db] *= a0;
+            o1[db] *= a1;
+          }
+          l0 *= a0;
+          l1 *= a1;
+          m0 = n0;
+          m1 = n1;
+        }
+        const float mb0 = (m0 == -INFINITY) ? 0.f : m0;
+        const float mb1 = (m1 == -INFINITY) ? 0.f : m1;
+        bf16x8 p0[2], p1[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p0[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(s0[i], c, -mb0));
+          p1[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(s1[i], c, -mb1));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            l0 = dot2_ones(bf16x2{p0[ks][j], p0[ks][j + 1]}, l0);
+            l1 = dot2_ones(bf16x2{p1[ks][j], p1[ks][j + 1]}, l1);
+          }
+        }
+        // ---- O^T += V^T P^T
+        const int i16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int row = kb * 32 + 16 * ks + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) {
+            const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+            const bf16x4 va = lds_read_tr4(&Vt[v_phys<D>(row, col)]);
+            const bf16x4 vb = lds_read_tr4(&Vt[v_phys<D>(row + 8, col)]);
+            const bf16x8 vv = concat(va, vb);
+            o0[db] = mfma32(vv, p0[ks], o0[db]);
+            o1[db] = mfma32(vv, p1[ks], o1[db]);
+          }
+        }
+      }
+    }
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // ---- epilogue: normalise, subtract lambda * head 2, optional RMSNorm, store
+  l0 += partner32(l0, lo);
+  l1 += partner32(l1, lo);
+  const int qi = i0 + l32;
+  const bool ok = qi < T;
+  const float lamv = ok ? a.lam[((size_t)b * T + qi) * a.P + p] : 0.f;
+  const float inv0 = 1.0f / l0;
+  const float inv1 = lamv / l1;
+  float ss = 0.f;
+  {
+    // Both products are rounded before the subtraction (FMA contraction off), so
+    // the two branches are treated alike and identical branches with lambda = 1
+    // cancel exactly.
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = o0[db][i] * inv0 - o1[db][i] * inv1;
+        o0[db][i] = x;
+        ss += x * x;
+      }
+    }
+  }
+  if (a.v1) {
+    ss += partner32(ss, lo);
+    const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o0[db] *= r;
+  }
+  if (!ok) return;
+  bf16* dst = a.out + (((size_t)b * T + qi) * a.P + p) * D + 4 * (lane >> 5);
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (bf16)o0[db][4 * i4 + e];
+      *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * i4) = w;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch(const PrefillProblem& pr, hipStream_t s) {
+  Args a;
+  a.q = static_cast<const bf16*>(pr.q);
+  a.k = static_cast<const bf16*>(pr.k);
+  a.v = static_cast<const bf16*>(pr.v);
+  a.lam = pr.lam;
+  a.out = static_cast<bf16*>(pr.out);
+  a.B = pr.B;
+  a.T = pr.T;
+  a.Hq = pr.Hq;
+  a.Hkv = pr.Hkv;
+  a.G = pr.Hq / (2 * pr.Hkv);
+  a.P = pr.Hq / 2;
+  a.causal = pr.causal ? 1 : 0;
+  a.v1 = pr.v1_rmsnorm ? 1 : 0;
+  a.eps = pr.eps;
+  a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  a.ppw = a.G < WAVES ? a.G : WAVES;
+  a.nsub = WAVES / a.ppw;
+  a.chunks = (a.G + a.ppw - 1) / a.ppw;
+  const int tokens_wg = QB * a.nsub;
+  a.ntb = (a.T + tokens_wg - 1) / tokens_wg;
+  a.units = a.B * a.Hkv * a.chunks;
+  const long long blocks = (long long)a.ntb * a.units;
+  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)blocks), dim3(THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillProblem& p, hipStream_t s) {
+  return p.d == 128 ? launch<128>(p, s) : launch<64>(p, s);
+}
+
+}  // namespace diffattn

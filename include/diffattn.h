@@ -1,0 +1,129 @@
+/*
+ * libdiffattn -- Differential Attention V2 forward pass for AMD MI355X (gfx950).
+ *
+ * The operation (sources: the web pages on Differential Transformer V2):
+ *   For each batch b, differential pair p and query token i, with the pair's two
+ *   query heads h1 = 2p and h2 = 2p+1 sharing one K/V head g = p / G
+ *   (G = Hq / (2*Hkv) pairs per KV head):
+ *       A_r = softmax(q[b,i,h_r] . K[b,:,g]^T / sqrt(d))     r = 1, 2
+ *       out[b,i,p,:] = A_1 V[b,:,g] - lambda[b,i,p] * A_2 V[b,:,g]
+ *   -- the differential map (A1 - lambda A2) V: lesson "差异性注意力 (V2)"
+ *   (AI Engineering from Scratch, phase 10), section "概念 / 差异性概念", computed
+ *   as A1 V - lambda A2 V; the V2 head layout (query heads doubled, adjacent query
+ *   heads of one GQA group share K/V and the head dim, KV heads unchanged): article
+ *   "Differential Transformer V2 soll KI-Training stabiler machen"
+ *   (dailytechsnack.ch), section "Gemeinsamer KV-Cache statt Spezialkernel";
+ *   lambda per token and head, sigmoid-bounded: same article, section "Weniger
+ *   Ausreisser und Gradientenspitzen"; causal mask j <= i: lesson "注意 变量"
+ *   (phase 7, attention variants), "建立它 / 步骤1".
+ *   V1 reference mode (flag DIFFATTN_FLAG_V1_RMSNORM): out = x / sqrt(mean_c x_c^2 + eps)
+ *   per output head, applied after the difference -- differential-attention lesson,
+ *   "关键词" (per-head RMSNorm).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the library
+ *     never allocates, frees, or keeps them, and never synchronises.  Work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the legacy default stream) and
+ *     completes asynchronously.  Outputs must not alias inputs.
+ *   - Element types: dtype DIFFATTN_BF16 (q/k/v/out are bf16, fp32 accumulation)
+ *     or DIFFATTN_FP32 (q/k/v/out are fp32).  lambda is always fp32.
+ *   - Layouts are row-major with the head dim fastest ("BTHD").
+ *   - Supported: d in {64, 128}; Hq a multiple of 2*Hkv; G = Hq/(2*Hkv) <= 8.
+ *   - Errors: arguments are validated on the host before anything is enqueued;
+ *     on error nothing is written and a nonzero diffattn_status_t is returned.
+ *     Device pointers must be non-NULL and 16-byte aligned.  A failed kernel
+ *     launch returns DIFFATTN_ERR_HIP; faults inside a kernel surface at the
+ *     caller's next synchronisation, as with any HIP call.
+ *   - Thread safety: the library is stateless; concurrent calls are safe.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIFFATTN_OK = 0,
+  DIFFATTN_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, non-positive size, bad ratio, overflow */
+  DIFFATTN_ERR_UNSUPPORTED = 2, /* valid but not built: head dim, group size, dtype */
+  DIFFATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  DIFFATTN_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} diffattn_status_t;
+
+typedef enum { DIFFATTN_BF16 = 0, DIFFATTN_FP32 = 1 } diffattn_dtype_t;
+
+/* V1 reference mode: per-head RMSNorm (no gain) of the differential output. */
+#define DIFFATTN_FLAG_V1_RMSNORM 0x1u
+
+/*
+ * Prefill: differential attention over a whole sequence.
+ *   q      device [B, T, Hq, d]   (dtype)
+ *   k, v   device [B, T, Hkv, d]  (dtype)
+ *   lambda device [B, T, P] fp32, P = Hq/2; used as given (V2 callers pass
+ *          sigmoid outputs; any real value is accepted, as V1's lambda may be < 0)
+ *   out    device [B, T, P, d]    (dtype), fully overwritten
+ *   causal nonzero: key j visible to query i iff j <= i; zero: all T keys visible
+ *   flags  0 or DIFFATTN_FLAG_V1_RMSNORM; rms_eps used only with that flag (> 0)
+ * Returns a diffattn_status_t.
+ */
+int diffattn_prefill_fwd(const void* q, const void* k, const void* v, const float* lambda, void* out,
+                         int B, int T, int Hq, int Hkv, int d, int causal,
+                         int dtype, unsigned flags, float rms_eps, void* stream);
+
+/*
+ * Decode: one new query token per sequence against a contiguous KV cache that
+ * already holds that token (the query sits at position L-1 and sees all L rows).
+ * Each cache byte is read from HBM once per KV-head group (both heads of every
+ * pair in the group share it), split over `num_splits` key ranges whose partial
+ * softmax states are merged by a second kernel.
+ *   q        device [B, Hq, d]       (dtype)
+ *   k_cache  device [B, L, Hkv, d]   (dtype)
+ *   v_cache  device [B, L, Hkv, d]   (dtype)
+ *   lambda   device [B, P] fp32
+ *   out      device [B, P, d]        (dtype), fully overwritten
+ *   num_splits  key-range splits per (b, KV head); 0 = library's choice
+ *               (diffattn_decode_num_splits); clamped to [1, ceil(L/32)]
+ *   workspace   device scratch, >= diffattn_decode_workspace_bytes(...) bytes,
+ *               16-byte aligned; contents on entry are ignored
+ * Returns a diffattn_status_t.
+ */
+int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
+                        void* out, int B, int L, int Hq, int Hkv, int d,
+                        int dtype, unsigned flags, float rms_eps, int num_splits,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split count the library picks for a decode problem (host only; no GPU call).
+ * Returns 0 on invalid sizes. */
+int diffattn_decode_num_splits(int B, int L, int Hq, int Hkv, int d);
+
+/* Workspace bytes diffattn_decode_fwd needs for these sizes and num_splits
+ * (0 = library's choice).  Host only; returns 0 on invalid sizes. */
+size_t diffattn_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int d, int num_splits);
+
+/*
+ * V1 reference-mode lambda, one value per differential pair, broadcast over rows:
+ *   lambda_out[r, p] = exp(lq1[p].lk1[p]) - exp(lq2[p].lk2[p]) + lambda_init
+ * (differential-attention lesson, "概念 / 差异性概念": the lambda re-parameterisation;
+ * lambda_init a small positive number such as 0.8).
+ *   lq1, lk1, lq2, lk2  device [P, d_lambda] fp32
+ *   lambda_out          device [rows, P] fp32 (rows = B*T for prefill, B for decode)
+ * Returns a diffattn_status_t.
+ */
+int diffattn_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
+                       float lambda_init, float* lambda_out, int P, int d_lambda, int rows,
+                       void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* diffattn_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int diffattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

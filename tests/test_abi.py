@@ -1,0 +1,140 @@
+"""libdiffattn C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects invalid arguments on the host before any HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from differential_attention_v2_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diffattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from differential_attention_v2_amd import build_lib
+        build_lib.build()
+    return bd.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"diffattn_prefill_fwd", "diffattn_decode_fwd", "diffattn_decode_workspace_bytes",
+            "diffattn_decode_num_splits", "diffattn_v1_lambda", "diffattn_status_string",
+            "diffattn_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in bd._SIGNATURES, f"binding lacks {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert bd.diffattn_version() == 100
+    for st in range(5):
+        assert bd.status_string(st)
+    assert bd.status_string(99) == "unknown status"
+
+
+# a fake, 256-byte aligned "device" address: never dereferenced, every call
+# below fails validation on another argument first
+P = 0x7F0000000000
+
+
+def _prefill(**kw):
+    a = dict(q=P, k=P, v=P, lam=P, out=P, B=1, T=16, Hq=8, Hkv=2, d=128, causal=1, dtype=0, flags=0,
+             rms_eps=1e-5, stream=None)
+    a.update(kw)
+    return bd.diffattn_prefill_fwd(**a)
+
+
+def _decode(**kw):
+    a = dict(q=P, k_cache=P, v_cache=P, lam=P, out=P, B=2, L=100, Hq=8, Hkv=2, d=128, dtype=0, flags=0,
+             rms_eps=1e-5, num_splits=0, workspace=None, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return bd.diffattn_decode_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(out=None), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(lam=None), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(k=P + 8), bd.DIFFATTN_ERR_INVALID_ARG),          # not 16-byte aligned
+    (dict(lam=P + 2), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(B=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(T=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(T=-5), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=2), bd.DIFFATTN_ERR_INVALID_ARG),      # Hq not a multiple of 2*Hkv
+    (dict(Hq=8, Hkv=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(d=96), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(d=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(Hq=36, Hkv=2), bd.DIFFATTN_ERR_UNSUPPORTED),     # G = 9 pairs per KV head
+    (dict(dtype=7), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(flags=0x4), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(flags=1, rms_eps=0.0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(flags=1, rms_eps=float("nan")), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(B=1 << 20, T=1 << 20), bd.DIFFATTN_ERR_INVALID_ARG),   # element count overflow
+])
+def test_prefill_rejects(lib, kw, status):
+    assert _prefill(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(v_cache=P + 4), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(L=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(num_splits=-1), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(d=32), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(Hq=10, Hkv=2), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(flags=1, rms_eps=-1.0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(workspace=None, workspace_bytes=1 << 30), bd.DIFFATTN_ERR_WORKSPACE),
+    (dict(workspace=P, workspace_bytes=16), bd.DIFFATTN_ERR_WORKSPACE),
+    (dict(workspace=P + 8, workspace_bytes=1 << 30), bd.DIFFATTN_ERR_WORKSPACE),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _decode(**kw) == status
+
+
+def test_v1_lambda_rejects(lib):
+    assert bd.diffattn_v1_lambda(None, P, P, P, 0.8, P, 4, 128, 1, None) == bd.DIFFATTN_ERR_INVALID_ARG
+    assert bd.diffattn_v1_lambda(P, P, P, P, 0.8, P, 0, 128, 1, None) == bd.DIFFATTN_ERR_INVALID_ARG
+    assert bd.diffattn_v1_lambda(P, P, P, P, float("inf"), P, 4, 128, 1, None) == bd.DIFFATTN_ERR_INVALID_ARG
+
+
+def test_decode_split_plan(lib):
+    # B*Hkv (b, KV head) units are split so that ~4096 waves stream the cache
+    assert bd.diffattn_decode_num_splits(64, 8192, 64, 8, 128) == 8
+    assert bd.diffattn_decode_num_splits(8, 131072, 64, 8, 128) == 64
+    assert bd.diffattn_decode_num_splits(1, 1, 2, 1, 64) == 1
+    assert bd.diffattn_decode_num_splits(1, 100, 2, 1, 64) == 4       # ceil(100/32) ranges of 32
+    assert bd.diffattn_decode_num_splits(1, 100, 3, 1, 64) == 0       # invalid heads
+    rec = 128 + 4
+    assert bd.diffattn_decode_workspace_bytes(64, 8192, 64, 8, 128, 0) == 64 * 64 * 8 * rec * 4
+    assert bd.diffattn_decode_workspace_bytes(8, 131072, 64, 8, 128, 0) == 8 * 64 * 64 * rec * 4
+    # explicit split counts are clamped to the number of 32-key blocks and never leave a range empty
+    assert bd.diffattn_decode_workspace_bytes(1, 100, 2, 1, 64, 1000) == 1 * 2 * 4 * (64 + 4) * 4
+    assert bd.diffattn_decode_workspace_bytes(1, 100, 2, 1, 64, 3) == 1 * 2 * 2 * (64 + 4) * 4   # chunk 64 -> 2
+    assert bd.diffattn_decode_workspace_bytes(0, 100, 2, 1, 64, 0) == 0
+
+
+def test_binding_refuses_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(bd, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        bd.load_library(str(tmp_path / "nope.so"))
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "differential_attention_v2_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
+                assert "diffattn_oracle" not in text, f

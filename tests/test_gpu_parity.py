@@ -1,0 +1,241 @@
+"""HIP path vs the fp64 oracle on identical seeded inputs (needs an MI355X).
+
+Every call goes through libdiffattn's C ABI (via the ctypes binding).  Bar:
+max-abs <= 2e-2 and mean-abs <= 2e-3 for bf16 inputs with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differential_attention_v2_amd import binding as bd
+from differential_attention_v2_amd import workloads as W
+
+from _helpers import assert_parity, from_device, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _f64(x, dtype):
+    return W.to_f64(x, dtype)
+
+
+def _prefill_case(w: W.Workload, dev, rows=None, v1=False, eps=1e-5):
+    inp = W.make_prefill(w)
+    q, k, v = (to_device(inp[n], w.dtype, dev) for n in ("q", "k", "v"))
+    lam = torch.from_numpy(inp["lam"]).to(dev)
+    out = from_device(bd.prefill(q, k, v, lam, causal=w.causal, v1_rmsnorm=v1, eps=eps))
+    ref = oracle.diffattn_prefill(_f64(inp["q"], w.dtype), _f64(inp["k"], w.dtype), _f64(inp["v"], w.dtype),
+                                  inp["lam"], causal=w.causal, v1_rmsnorm=v1, eps=eps, rows=rows)
+    got = out if rows is None else out[:, rows]
+    return got, ref
+
+
+def _decode_case(w: W.Workload, dev, batches=None, pairs=None, splits=0, v1=False, eps=1e-5, lam=None):
+    inp = W.make_decode(w)
+    q, k, v = (to_device(inp[n], w.dtype, dev) for n in ("q", "k", "v"))
+    lam_np = inp["lam"] if lam is None else lam
+    lam_t = torch.from_numpy(np.ascontiguousarray(lam_np, dtype=np.float32)).to(dev)
+    out = from_device(bd.decode(q, k, v, lam_t, v1_rmsnorm=v1, eps=eps, num_splits=splits))
+    b = np.arange(w.B) if batches is None else np.asarray(batches)
+    p = np.arange(w.P) if pairs is None else np.asarray(pairs)
+    ref = oracle.diffattn_decode(_f64(inp["q"], w.dtype), _f64(inp["k"], w.dtype), _f64(inp["v"], w.dtype),
+                                 lam_np, v1_rmsnorm=v1, eps=eps, batches=b, pairs=p)
+    return out[np.ix_(b, p)], ref
+
+
+# ------------------------------------------------------------------ the five workloads
+def test_c1_tiny_fp32(gpu_device):
+    got, ref = _prefill_case(W.CONFIGS[1], gpu_device)
+    err = assert_parity(got, ref, "c1 fp32 T=128")
+    assert err["max_abs"] < 1e-4     # fp32 all the way
+
+
+def test_c2_prefill_full(gpu_device):
+    got, ref = _prefill_case(W.CONFIGS[2], gpu_device)
+    assert_parity(got, ref, "c2 bf16 T=4096 all rows")
+
+
+def _c3_rows(T, seed=3):
+    rng = np.random.default_rng(seed)
+    edges = np.concatenate([[t - 1, t] for t in range(64, T, 4096)])
+    rows = np.concatenate([np.arange(128), np.arange(T - 128, T), edges, rng.choice(T, 256, replace=False)])
+    return np.unique(rows[(rows >= 0) & (rows < T)])
+
+
+def test_c3_prefill_sampled_rows(gpu_device):
+    w = W.CONFIGS[3]
+    rows = _c3_rows(w.T)
+    got, ref = _prefill_case(w, gpu_device, rows=rows)
+    assert_parity(got, ref, f"c3 bf16 T=32768 ({rows.size} sampled rows, all pairs)")
+
+
+def test_c4_decode(gpu_device):
+    w = W.CONFIGS[4]
+    got, ref = _decode_case(w, gpu_device, batches=[0, 1, 13, 31, 32, 47, 62, 63])
+    assert_parity(got, ref, "c4 decode B=64 L=8192 (8 batches, all pairs)")
+
+
+def test_c5_decode_and_v1_mode(gpu_device):
+    w = W.CONFIGS[5]
+    b, p = [0, 5], [0, 9, 18, 31]
+    got, ref = _decode_case(w, gpu_device, batches=b, pairs=p)
+    assert_parity(got, ref, "c5 decode B=8 L=131072")
+    vec = W.make_v1_lambda_vectors(w.P)
+    lam1 = oracle.v1_lambda(vec["lq1"], vec["lk1"], vec["lq2"], vec["lk2"], 0.8)
+    # the V1 lambda through the library's own kernel, checked against the oracle
+    dv = {n: torch.from_numpy(vec[n]).to(gpu_device) for n in vec}
+    lam_dev = bd.v1_lambda(dv["lq1"], dv["lk1"], dv["lq2"], dv["lk2"], 0.8, rows=w.B)
+    np.testing.assert_allclose(lam_dev.cpu().numpy(), np.broadcast_to(lam1, (w.B, w.P)), rtol=2e-6, atol=2e-6)
+    got, ref = _decode_case(w, gpu_device, batches=b, pairs=p, v1=True, eps=1e-5,
+                            lam=lam_dev.cpu().numpy())
+    assert_parity(got, ref, "c5 decode V1 mode (exp-dot lambda, RMSNorm eps=1e-5)")
+
+
+# ------------------------------------------------------------------ edge shapes
+PREFILL_EDGES = [
+    # B, T, Hq, Hkv, d, causal
+    (1, 1, 8, 1, 128, True),
+    (2, 2, 8, 2, 128, True),
+    (1, 63, 16, 2, 128, True),
+    (1, 65, 8, 4, 64, True),
+    (2, 127, 8, 1, 128, False),
+    (1, 129, 16, 1, 64, True),      # G = 8
+    (1, 200, 4, 1, 128, False),     # G = 2
+    (3, 97, 12, 2, 64, True),       # G = 3
+    (1, 300, 2, 1, 128, True),      # G = 1
+    (2, 1000, 64, 8, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,d,causal", PREFILL_EDGES)
+def test_prefill_edges(gpu_device, B, T, Hq, Hkv, d, causal):
+    w = W.Workload("edge", "prefill", "bf16", B=B, T=T, Hq=Hq, Hkv=Hkv, d=d, qkv_scale=0.7071,
+                   causal=causal, seed=77 + T)
+    got, ref = _prefill_case(w, gpu_device)
+    assert_parity(got, ref, f"prefill edge {B,T,Hq,Hkv,d,causal}")
+
+
+def test_prefill_fp32_d128_noncausal(gpu_device):
+    w = W.Workload("edge32", "prefill", "fp32", B=2, T=70, Hq=8, Hkv=2, d=128, causal=False, seed=5)
+    got, ref = _prefill_case(w, gpu_device)
+    assert assert_parity(got, ref, "fp32 prefill d=128 non-causal")["max_abs"] < 1e-4
+
+
+DECODE_EDGES = [
+    # B, L, Hq, Hkv, d, splits
+    (1, 1, 8, 1, 128, 0),
+    (2, 31, 8, 2, 128, 0),
+    (3, 33, 16, 1, 64, 3),
+    (2, 1000, 8, 4, 128, 7),
+    (1, 4097, 12, 2, 64, 0),
+    (2, 5000, 2, 1, 128, 1),
+    (4, 2048, 64, 8, 128, 0),
+]
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,d,splits", DECODE_EDGES)
+def test_decode_edges(gpu_device, B, L, Hq, Hkv, d, splits):
+    w = W.Workload("dedge", "decode", "bf16", B=B, T=L, Hq=Hq, Hkv=Hkv, d=d, seed=91 + L)
+    got, ref = _decode_case(w, gpu_device, splits=splits)
+    assert_parity(got, ref, f"decode edge {B,L,Hq,Hkv,d,splits}")
+
+
+def test_decode_fp32(gpu_device):
+    w = W.Workload("d32", "decode", "fp32", B=2, T=300, Hq=8, Hkv=2, d=64, seed=8)
+    got, ref = _decode_case(w, gpu_device)
+    assert assert_parity(got, ref, "fp32 decode")["max_abs"] < 1e-4
+
+
+# ------------------------------------------------------------------ cross-path and invariants
+def test_decode_split_count_invariance(gpu_device):
+    w = W.Workload("split", "decode", "bf16", B=2, T=4096, Hq=16, Hkv=2, d=128, seed=12)
+    outs = []
+    for s in (1, 4, 16, 128):
+        got, ref = _decode_case(w, gpu_device, splits=s)
+        assert_parity(got, ref, f"decode splits={s}")
+        outs.append(got)
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() < 1e-2
+
+
+def test_decode_equals_last_prefill_row(gpu_device):
+    dev = gpu_device
+    w = W.Workload("x", "prefill", "bf16", B=2, T=777, Hq=16, Hkv=2, d=128, qkv_scale=1.0, seed=21)
+    inp = W.make_prefill(w)
+    q, k, v = (to_device(inp[n], "bf16", dev) for n in ("q", "k", "v"))
+    lam = torch.from_numpy(inp["lam"]).to(dev)
+    pre = from_device(bd.prefill(q, k, v, lam))[:, -1]
+    dec = from_device(bd.decode(q[:, -1].contiguous(), k, v, lam[:, -1].contiguous()))
+    assert np.abs(pre - dec).max() < 1e-2
+    ref = oracle.diffattn_prefill(_f64(inp["q"], "bf16"), _f64(inp["k"], "bf16"), _f64(inp["v"], "bf16"),
+                                  inp["lam"], rows=[w.T - 1])[:, 0]
+    assert_parity(dec, ref, "decode(L) vs oracle prefill row L-1")
+
+
+def test_identical_branches_cancel_exactly(gpu_device):
+    dev = gpu_device
+    w = W.Workload("z", "prefill", "bf16", B=1, T=333, Hq=16, Hkv=2, d=128, seed=31)
+    inp = W.make_prefill(w)
+    qn = inp["q"].copy()
+    qn[:, :, 1::2] = qn[:, :, 0::2]
+    q, k, v = to_device(qn, "bf16", dev), to_device(inp["k"], "bf16", dev), to_device(inp["v"], "bf16", dev)
+    ones = torch.ones((1, w.T, w.P), dtype=torch.float32, device=dev)
+    assert torch.count_nonzero(bd.prefill(q, k, v, ones)).item() == 0
+    assert torch.count_nonzero(bd.decode(q[:, -1].contiguous(), k, v, ones[:, -1].contiguous())).item() == 0
+
+
+def test_deterministic(gpu_device):
+    dev = gpu_device
+    w = W.CONFIGS[2].with_(T=1024)
+    inp = W.make_prefill(w)
+    q, k, v = (to_device(inp[n], "bf16", dev) for n in ("q", "k", "v"))
+    lam = torch.from_numpy(inp["lam"]).to(dev)
+    a = bd.prefill(q, k, v, lam)
+    b = bd.prefill(q, k, v, lam)
+    assert torch.equal(a, b)
+    da = bd.decode(q[:, -1].contiguous(), k, v, lam[:, -1].contiguous())
+    db = bd.decode(q[:, -1].contiguous(), k, v, lam[:, -1].contiguous())
+    assert torch.equal(da, db)
+
+
+def test_v1_mode_prefill(gpu_device):
+    """V1 mode normalises each output head to unit RMS, so its absolute error scales with y itself.
+
+    The bar is applied where it was stated, at the scale of the differential
+    output x: y_gpu * sqrt(mean(x_ref^2) + eps) against x_ref.  The normalised
+    output itself must match to rel-L2 <= 1e-2.
+    """
+    w = W.CONFIGS[2].with_(T=512, seed=44)
+    eps = 1e-5
+    inp = W.make_prefill(w)
+    dev = gpu_device
+    q, k, v = (to_device(inp[n], "bf16", dev) for n in ("q", "k", "v"))
+    y = from_device(bd.prefill(q, k, v, torch.from_numpy(inp["lam"]).to(dev), v1_rmsnorm=True, eps=eps))
+    f = [W.to_f64(inp[n], "bf16") for n in ("q", "k", "v")]
+    x_ref = oracle.diffattn_prefill(*f, inp["lam"])
+    y_ref = oracle.diffattn_prefill(*f, inp["lam"], v1_rmsnorm=True, eps=eps)
+    r_ref = np.sqrt(np.mean(x_ref * x_ref, axis=-1, keepdims=True) + eps)
+    assert_parity(y * r_ref, x_ref, "V1 mode prefill T=512, at the scale of x")
+    err = assert_parity(y, y_ref, "V1 mode prefill T=512, normalised", max_abs=6e-2, mean_abs=6e-3)
+    assert err["rel_l2"] <= 1e-2
+
+
+def test_noncausal_matches_oracle_c2_shape(gpu_device):
+    w = W.CONFIGS[2].with_(T=640, causal=False, seed=45)
+    got, ref = _prefill_case(w, gpu_device)
+    assert_parity(got, ref, "non-causal prefill T=640")
+
+
+def test_nan_in_one_query_row_stays_in_that_row(gpu_device):
+    dev = gpu_device
+    w = W.Workload("nan", "prefill", "bf16", B=1, T=100, Hq=8, Hkv=1, d=128, seed=50)
+    inp = W.make_prefill(w)
+    qn = inp["q"].copy()
+    qn[0, 40, 2] = 0x7FC0      # bf16 NaN in query row 40, head 2 (pair 1, branch 1)
+    q, k, v = to_device(qn, "bf16", dev), to_device(inp["k"], "bf16", dev), to_device(inp["v"], "bf16", dev)
+    out = from_device(bd.prefill(q, k, v, torch.from_numpy(inp["lam"]).to(dev)))
+    bad = ~np.isfinite(out)
+    assert bad[0, 40, 1].all()
+    bad[0, 40, 1] = False
+    assert not bad.any()
