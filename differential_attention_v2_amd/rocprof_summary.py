@@ -1,0 +1,127 @@
+"""Summarise rocprofv3 CSV output into short text reports and HBM-traffic records.
+
+    # kernel-trace statistics (from rocprofv3 --kernel-trace --stats --output-format csv)
+    python -m differential_attention_v2_amd.rocprof_summary stats DIR/run_kernel_stats.csv \
+        --cmd "<the rocprofv3 command>" --title "..." --out profiles/NAME.txt
+
+    # HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE runs, scaled by what the
+    # same counters read for a plain device copy of known size
+    python -m differential_attention_v2_amd.rocprof_summary traffic \
+        --fetch DIR/run_counter_collection.csv --write DIR/run_counter_collection.csv \
+        --copy-fetch DIR/... --copy-write DIR/... --copy-bytes N \
+        --kernel prefill=prefill_kernel<128>:prefill_bf16.hip,dev_common.h:ALGO_BYTES \
+        --cmd "..." --out profiles/NAME.txt --json profiles/traffic.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "differential_attention_v2_amd", "csrc")
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    name = name.replace("diffattn::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    return name.split("(")[0].replace("void ", "")
+
+
+def cmd_stats(a) -> None:
+    rows = list(csv.DictReader(open(a.csv)))
+    lines = [f"# {a.title}", "", "command:", f"  {a.cmd}", "",
+             f"{'kernel':48s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share%':>7s}"]
+    for r in rows:
+        lines.append(f"{_short(r['Name'])[:48]:48s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
+                     f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} {float(r['Percentage']):7.2f}")
+    if a.note:
+        lines += ["", a.note]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _per_kernel(path: str) -> dict:
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        vals.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def cmd_traffic(a) -> None:
+    n = a.copy_bytes / 1024.0   # KiB moved each way by one copy dispatch
+    cf = _per_kernel(a.copy_fetch)
+    cw = _per_kernel(a.copy_write)
+    copy_name = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()][0]
+    f_fetch = n / statistics.median(cf[copy_name])
+    f_write = n / statistics.median(cw[copy_name])
+    fe, wr = _per_kernel(a.fetch), _per_kernel(a.write)
+    lines = [f"# {a.title}", "", "commands:"] + [f"  {c}" for c in a.cmd] + [
+        "", f"calibration: copy of {a.copy_bytes} B per dispatch: FETCH_SIZE reads "
+            f"{statistics.median(cf[copy_name]):.1f} KiB (factor {f_fetch:.4f}), WRITE_SIZE reads "
+            f"{statistics.median(cw[copy_name]):.1f} KiB (factor {f_write:.4f})", "",
+        f"{'kernel':40s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} {'read MB':>10s} {'write MB':>10s} {'algo MB':>10s}"]
+    out = json.load(open(a.json)) if (a.json and os.path.exists(a.json)) else {}
+    for spec in a.kernel:
+        key, rest = spec.split("=", 1)
+        names, srcs, algo = rest.split(":")
+        total_r = total_w = 0.0
+        for kname in names.split("+"):
+            match = [k for k in fe if k.startswith(kname)]
+            if not match:
+                raise SystemExit(f"kernel {kname} not in counter data: {list(fe)}")
+            k = match[0]
+            fk, wk = statistics.median(fe[k]), statistics.median(wr[k])
+            rb, wb = fk * f_fetch * 1024, wk * f_write * 1024
+            total_r += rb
+            total_w += wb
+            lines.append(f"{kname[:40]:40s} {fk:12.1f} {wk:12.1f} {rb/1e6:10.2f} {wb/1e6:10.2f} {'':>10s}")
+        lines.append(f"{'  = ' + key + ' per launch':40s} {'':12s} {'':12s} {total_r/1e6:10.2f} {total_w/1e6:10.2f} "
+                     f"{float(algo)/1e6:10.2f}")
+        src_list = srcs.split(",")
+        out[key] = {"kernels": names.split("+"), "sources": src_list, "source_hash": source_hash(src_list),
+                    "read_bytes_per_launch": total_r, "write_bytes_per_launch": total_w,
+                    "bytes_per_launch": total_r + total_w, "algorithmic_bytes": float(algo),
+                    "fetch_factor": f_fetch, "write_factor": f_write}
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    if a.json:
+        json.dump(out, open(a.json, "w"), indent=1)
+    print("\n".join(lines))
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--note", default="")
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for n in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + n.replace("_", "-"), dest=n, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--kernel", action="append", required=True,
+                   help="key=name[+name]:src[,src]:algorithmic_bytes")
+    t.add_argument("--cmd", action="append", required=True)
+    t.add_argument("--title", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--json", default=None)
+    a = ap.parse_args(argv)
+    cmd_stats(a) if a.what == "stats" else cmd_traffic(a)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
