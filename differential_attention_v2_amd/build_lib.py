@@ -26,8 +26,12 @@ SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip"]
 
 # Packed-fp32 VALU instructions are kept out of every kernel; hipcc -O3 would
 # otherwise form them from plain float code.
+# MFMA results are selected into VGPRs (not AGPRs): the online-softmax rescale
+# multiplies the accumulators with VALU ops, and AGPR accumulators made the
+# compiler copy them between register files on every tile.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-command-line-argument"]
 
 

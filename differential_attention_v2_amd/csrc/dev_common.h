@@ -65,6 +65,20 @@ __device__ __forceinline__ float dot2_ones(bf16x2 p, float acc) {
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l (lds_base wave-uniform).  Issued as inline asm so the compiler
+// does not insert conservative vmcnt waits in front of unrelated LDS reads; the
+// caller waits with wait_vmcnt0() before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)LDS_PTR(const char, lds_base);
+  // one wait state between the M0 write and the LDS-DMA load that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0) as a builtin (expcnt/lgkmcnt left at their maxima), visible to the
+// compiler's own wait-count tracking: loads issued before it need no later wait.
+__device__ __forceinline__ void wait_vmcnt0_builtin() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void sts16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace diffattn

@@ -14,7 +14,9 @@
 // group and 32 query tokens, i.e. 64 query rows (32 tokens x the pair's two
 // heads), so the lambda-subtract happens in registers.  Every K/V tile of 64
 // keys is copied from HBM/L2 into LDS once per workgroup and read by all waves:
-// with G = 4 pairs per KV head, one staged byte serves all 8 query heads.
+// with G = 4 pairs per KV head, one staged byte serves all 8 query heads.  The
+// copy uses the direct global-to-LDS loads (16 bytes per lane, no registers),
+// issued one tile ahead into the other half of a double buffer.
 //
 // Per 32-key half-tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (A = K from LDS, B = Q^T held in registers), so each lane holds the scores of
@@ -63,10 +65,12 @@ __device__ __forceinline__ int k_phys(int row, int col) {   // col in elements
   return row * D + ((((col >> 3) ^ (row & (NCH - 1)))) << 3) + (col & 7);
 }
 template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return (D >= 128) ? ((row & 3) << 2) : ((row & 1) << 2);
+}
+template <int D>
 __device__ __forceinline__ int v_phys(int row, int col) {
-  constexpr int NCH = D / 8;
-  const int sw = (NCH >= 16) ? ((row & 3) << 2) : ((row & 1) << 2);
-  return row * D + ((((col >> 3) ^ sw)) << 3) + (col & 7);
+  return row * D + ((((col >> 3) ^ v_swz<D>(row))) << 3) + (col & 7);
 }
 
 template <int D>
@@ -80,7 +84,9 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave index as a scalar, so everything derived from it (pair, first token,
+  // masking decisions) stays wave-uniform and compiles to scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool lo = lane < 32;
   const int l32 = lane & 31;
 
@@ -145,40 +151,33 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   float l0 = 0.f, l1 = 0.f;               // this lane's share of the softmax denominators
   const float c = a.scale_log2;
 
-  u32x4 kr[LOADS], vr[LOADS];
-  auto load_tile = [&](int t) {
+  // ---- direct global -> LDS tile copy.  Wave-instruction j of wave w fills the
+  // 64 consecutive 16-byte slots [(j*WAVES + w)*64, +64) of a tile; slot s holds
+  // row s/NCH, physical chunk s%NCH, i.e. logical chunk (s%NCH) ^ swizzle(row).
+  // Rows past the sequence end repeat the last row (finite data; masked out).
+  auto dma_tile = [&](int t, int buf) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int cid = tid + j * THREADS;
-      const int r = cid / NCH, ch = cid % NCH;
-      const int key = t * BN + r;
-      if (key < T) {
-        kr[j] = ldg16(kbase + key * kv_row + 8 * ch);
-        vr[j] = ldg16(vbase + key * kv_row + 8 * ch);
-      } else {
-        kr[j] = u32x4{0, 0, 0, 0};
-        vr[j] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const int cid = tid + j * THREADS;
-      const int r = cid / NCH, ch = cid % NCH;
-      sts16(&smem[buf][0][k_phys<D>(r, 8 * ch)], kr[j]);
-      sts16(&smem[buf][1][v_phys<D>(r, 8 * ch)], vr[j]);
+      const int blk = j * WAVES + wave;
+      const int slot = blk * 64 + lane;
+      const int r = slot / NCH, pc = slot % NCH;
+      const int key = min(t * BN + r, T - 1);
+      const size_t roff = (size_t)key * kv_row;
+      const int ck = pc ^ (r & (NCH - 1));
+      const int cv = pc ^ v_swz<D>(r);
+      dma16(kbase + roff + 8 * ck, &smem[buf][0][blk * 64 * 8]);
+      dma16(vbase + roff + 8 * cv, &smem[buf][1][blk * 64 * 8]);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
+  dma_tile(0, 0);
+  wait_vmcnt0_builtin();   // Q operands and the first tile have landed
   __syncthreads();
 
+  const int i16 = lane & 15, g16 = lane >> 4;
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
+    if (t + 1 < ntiles) dma_tile(t + 1, buf ^ 1);
 
     if (active) {
       const bf16* Kt = smem[buf][0];
@@ -189,15 +188,29 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
         if (kbase_tok >= T) break;
         if (a.causal && kbase_tok > i0 + QB - 1) break;
 
-        // ---- S^T = K Q^T for both heads (keys x queries)
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
+        // ---- S^T = K Q^T for both heads (keys x queries); all K operands read first
+        bf16x8 ka[KSTEPS];
         {
           const int r = kb * 32 + l32;
 #pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kt[k_phys<D>(r, 16 * s + 8 * (lane >> 5))]);
-            s0 = mfma32(ka, qreg[0][s], s0);
-            s1 = mfma32(ka, qreg[1][s], s1);
+          for (int s = 0; s < KSTEPS; ++s)
+            ka[s] = *reinterpret_cast<const bf16x8*>(&Kt[k_phys<D>(r, 16 * s + 8 * (lane >> 5))]);
+        }
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          s0 = mfma32(ka[s], qreg[0][s], s0);
+          s1 = mfma32(ka[s], qreg[1][s], s1);
+        }
+        // ---- V^T operands for this half tile, issued before the softmax
+        bf16x8 va[2][DBLK];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int row = kb * 32 + 16 * ks + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) {
+            const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+            va[ks][db] = concat(lds_read_tr4(&Vt[v_phys<D>(row, col)]), lds_read_tr4(&Vt[v_phys<D>(row + 8, col)]));
           }
         }
         // ---- masking: causal diagonal and sequence tail
@@ -254,24 +267,18 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
           }
         }
         // ---- O^T += V^T P^T
-        const int i16 = lane & 15, g16 = lane >> 4;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int row = kb * 32 + 16 * ks + 4 * (g16 >> 1) + (i16 >> 2);
 #pragma unroll
           for (int db = 0; db < DBLK; ++db) {
-            const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-            const bf16x4 va = lds_read_tr4(&Vt[v_phys<D>(row, col)]);
-            const bf16x4 vb = lds_read_tr4(&Vt[v_phys<D>(row + 8, col)]);
-            const bf16x8 vv = concat(va, vb);
-            o0[db] = mfma32(vv, p0[ks], o0[db]);
-            o1[db] = mfma32(vv, p1[ks], o1[db]);
+            o0[db] = mfma32(va[ks][db], p0[ks], o0[db]);
+            o1[db] = mfma32(va[ks][db], p1[ks], o1[db]);
           }
         }
       }
     }
 
-    if (more) store_tile(buf ^ 1);
+    wait_vmcnt0();
     __syncthreads();
   }
 
