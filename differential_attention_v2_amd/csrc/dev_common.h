@@ -75,7 +75,17 @@ __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
   // one wait state between the M0 write and the LDS-DMA load that reads it
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
 }
+// Same copy with a scalar 64-bit base and a per-lane 32-bit byte offset (the
+// "saddr" form): no per-lane 64-bit address arithmetic.  lds_addr is the
+// wave-uniform LDS byte address of lane 0's 16 bytes.
+__device__ __forceinline__ void dma16_saddr(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 // vmcnt(0) as a builtin (expcnt/lgkmcnt left at their maxima), visible to the
 // compiler's own wait-count tracking: loads issued before it need no later wait.
 __device__ __forceinline__ void wait_vmcnt0_builtin() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -29,6 +29,8 @@
 // O^T += V^T P^T; the V^T operand comes from the row-major V tile via the
 // transposing LDS read.  The epilogue normalises both heads, subtracts
 // lambda * head2 from head1 (optional V1 RMSNorm) and stores bf16.
+#include <type_traits>
+
 #include "dev_common.h"
 #include "internal.h"
 
@@ -73,6 +75,13 @@ __device__ __forceinline__ int v_phys(int row, int col) {
   return row * D + ((((col >> 3) ^ v_swz<D>(row))) << 3) + (col & 7);
 }
 
+__device__ __forceinline__ float max16(const f32x16& x) {
+  float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) m = fmaxf(fmaxf(m, x[i]), x[i + 1]);
+  return fmaxf(m, x[15]);
+}
+
 template <int D>
 __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   constexpr int NCH = D / 8;               // 16-byte chunks per row
@@ -80,7 +89,14 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   constexpr int DBLK = D / 32;             // PV output d-blocks
   constexpr int LOADS = BN * NCH / THREADS;  // 16-byte chunks per thread per tile (K or V)
   static_assert(LOADS >= 1 && (BN * NCH) % THREADS == 0, "tile/thread mismatch");
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * D];   // [buffer][K|V]
+  // K/V tiles triple-buffered: tile t lives in buffer t % NBUF and is requested
+  // two tiles ahead of its use, so its copy overlaps two tiles of compute.  The
+  // NBUF K buffers come first, then the NBUF V buffers, so every operand read is
+  // a per-lane offset plus a compile-time immediate.
+  constexpr int NBUF = 3;
+  constexpr int TILE_BYTES = BN * D * 2;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * NBUF * BN * D];
+  const char* lds = reinterpret_cast<const char*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,132 +170,172 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   // ---- direct global -> LDS tile copy.  Wave-instruction j of wave w fills the
   // 64 consecutive 16-byte slots [(j*WAVES + w)*64, +64) of a tile; slot s holds
   // row s/NCH, physical chunk s%NCH, i.e. logical chunk (s%NCH) ^ swizzle(row).
-  // Rows past the sequence end repeat the last row (finite data; masked out).
+  // Per lane the byte offset inside a tile of K (or V) rows is loop-invariant;
+  // the tile's base is a scalar.  Rows past the sequence end (last tile only)
+  // repeat the last row: finite data, always masked out.
+  const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
+  uint32_t dofs_k[LOADS], dofs_v[LOADS];
+  int drow[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int slot = (j * WAVES + wave) * 64 + lane;
+    const int r = slot / NCH, pc = slot % NCH;
+    drow[j] = r;
+    dofs_k[j] = r * row_bytes + 16 * (pc ^ (r & (NCH - 1)));
+    dofs_v[j] = r * row_bytes + 16 * (pc ^ v_swz<D>(r));
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)LDS_PTR(const char, lds);
   auto dma_tile = [&](int t, int buf) {
+    const char* kt = reinterpret_cast<const char*>(kbase) + (size_t)t * BN * row_bytes;
+    const char* vt = reinterpret_cast<const char*>(vbase) + (size_t)t * BN * row_bytes;
+    const bool tail = t * BN + BN > T;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int blk = j * WAVES + wave;
-      const int slot = blk * 64 + lane;
-      const int r = slot / NCH, pc = slot % NCH;
-      const int key = min(t * BN + r, T - 1);
-      const size_t roff = (size_t)key * kv_row;
-      const int ck = pc ^ (r & (NCH - 1));
-      const int cv = pc ^ v_swz<D>(r);
-      dma16(kbase + roff + 8 * ck, &smem[buf][0][blk * 64 * 8]);
-      dma16(vbase + roff + 8 * cv, &smem[buf][1][blk * 64 * 8]);
+      uint32_t ok = dofs_k[j], ov = dofs_v[j];
+      if (tail) {   // clamp rows past the end to the last row
+        const int back = max(0, t * BN + drow[j] - (T - 1));
+        ok -= back * row_bytes;
+        ov -= back * row_bytes;
+      }
+      const uint32_t dst = lds_base + (j * WAVES + wave) * 1024;
+      dma16_saddr(kt, ok, dst + buf * TILE_BYTES);
+      dma16_saddr(vt, ov, dst + (NBUF + buf) * TILE_BYTES);
     }
   };
 
-  dma_tile(0, 0);
-  wait_vmcnt0_builtin();   // Q operands and the first tile have landed
-  __syncthreads();
-
+  // ---- per-lane LDS read offsets (bytes), loop-invariant
   const int i16 = lane & 15, g16 = lane >> 4;
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) dma_tile(t + 1, buf ^ 1);
+  uint32_t kofs[KSTEPS];   // K rows as the A operand of S^T: row l32, k-step s
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+    kofs[s] = l32 * D * 2 + 16 * ((2 * s + (lane >> 5)) ^ (l32 & (NCH - 1)));
+  uint32_t vofs[DBLK];     // transposing reads of V for output d-block db
+  {
+    const int vrow = 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+      vofs[db] = NBUF * TILE_BYTES + 2 * v_phys<D>(vrow, col);
+    }
+  }
+  // (v_phys of row vrow + 16*ks + 8*r + 32*kb equals v_phys(vrow) + that many rows:
+  // the V swizzle depends on row % 4 only.)
 
-    if (active) {
-      const bf16* Kt = smem[buf][0];
-      const bf16* Vt = smem[buf][1];
+  auto compute_tile = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kbase_tok = t * BN + kb * 32;
-        if (kbase_tok >= T) break;
-        if (a.causal && kbase_tok > i0 + QB - 1) break;
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kbase_tok = t * BN + kb * 32;
+      if (kbase_tok >= T) break;
+      if (a.causal && kbase_tok > i0 + QB - 1) break;
 
-        // ---- S^T = K Q^T for both heads (keys x queries); all K operands read first
-        bf16x8 ka[KSTEPS];
-        {
-          const int r = kb * 32 + l32;
+      // ---- K operands and V^T operands of this half tile
+      bf16x8 ka[KSTEPS];
 #pragma unroll
-          for (int s = 0; s < KSTEPS; ++s)
-            ka[s] = *reinterpret_cast<const bf16x8*>(&Kt[k_phys<D>(r, 16 * s + 8 * (lane >> 5))]);
+      for (int s = 0; s < KSTEPS; ++s)
+        ka[s] = *reinterpret_cast<const bf16x8*>(lds + kofs[s] + BUF * TILE_BYTES + kb * 32 * D * 2);
+      bf16x8 va[2][DBLK];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const char* vp = lds + vofs[db] + BUF * TILE_BYTES + (kb * 32 + 16 * ks) * D * 2;
+          va[ks][db] = concat(lds_read_tr4(reinterpret_cast<const bf16*>(vp)),
+                              lds_read_tr4(reinterpret_cast<const bf16*>(vp + 8 * D * 2)));
         }
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
+      // ---- S^T = K Q^T (keys x queries), head 0's MFMAs then head 1's
+      const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          s0 = mfma32(ka[s], qreg[0][s], s0);
-          s1 = mfma32(ka[s], qreg[1][s], s1);
-        }
-        // ---- V^T operands for this half tile, issued before the softmax
-        bf16x8 va[2][DBLK];
+      for (int s = 0; s < KSTEPS; ++s) s0 = mfma32(ka[s], qreg[0][s], s0);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int row = kb * 32 + 16 * ks + 4 * (g16 >> 1) + (i16 >> 2);
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) {
-            const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-            va[ks][db] = concat(lds_read_tr4(&Vt[v_phys<D>(row, col)]), lds_read_tr4(&Vt[v_phys<D>(row + 8, col)]));
-          }
-        }
-        // ---- masking: causal diagonal and sequence tail
-        if ((a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T) {
-          const int qi = i0 + l32;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            const bool vis = key < T && (!a.causal || key <= qi);
-            if (!vis) {
-              s0[i] = -INFINITY;
-              s1[i] = -INFINITY;
-            }
-          }
-        }
-        // ---- online softmax, lazily rescaled
-        float mx0 = s0[0], mx1 = s1[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) {
-          mx0 = fmaxf(mx0, s0[i]);
-          mx1 = fmaxf(mx1, s1[i]);
-        }
-        mx0 = fmaxf(mx0, partner32(mx0, lo)) * c;
-        mx1 = fmaxf(mx1, partner32(mx1, lo)) * c;
-        const bool grow = (mx0 > m0 + RESCALE_LOG2) || (mx1 > m1 + RESCALE_LOG2);
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float n0 = fmaxf(m0, mx0), n1 = fmaxf(m1, mx1);
-          const float a0 = (n0 == -INFINITY) ? 1.f : fast_exp2(m0 - n0);
-          const float a1 = (n1 == -INFINITY) ? 1.f : fast_exp2(m1 - n1);
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) {
-            o0[db] *= a0;
-            o1[db] *= a1;
-          }
-          l0 *= a0;
-          l1 *= a1;
-          m0 = n0;
-          m1 = n1;
-        }
-        const float mb0 = (m0 == -INFINITY) ? 0.f : m0;
-        const float mb1 = (m1 == -INFINITY) ? 0.f : m1;
-        bf16x8 p0[2], p1[2];
+      for (int s = 0; s < KSTEPS; ++s) s1 = mfma32(ka[s], qreg[1][s], s1);
+      if (need_mask) {   // causal diagonal and sequence tail
+        const int qi = i0 + l32;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p0[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(s0[i], c, -mb0));
-          p1[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(s1[i], c, -mb1));
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            l0 = dot2_ones(bf16x2{p0[ks][j], p0[ks][j + 1]}, l0);
-            l1 = dot2_ones(bf16x2{p1[ks][j], p1[ks][j + 1]}, l1);
-          }
-        }
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) {
-            o0[db] = mfma32(va[ks][db], p0[ks], o0[db]);
-            o1[db] = mfma32(va[ks][db], p1[ks], o1[db]);
+          const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const bool vis = key < T && (!a.causal || key <= qi);
+          if (!vis) {
+            s0[i] = -INFINITY;
+            s1[i] = -INFINITY;
           }
         }
       }
+      // ---- online softmax, lazily rescaled
+      float mx0 = max16(s0), mx1 = max16(s1);
+      mx0 = fmaxf(mx0, partner32(mx0, lo)) * c;
+      mx1 = fmaxf(mx1, partner32(mx1, lo)) * c;
+      const bool grow = (mx0 > m0 + RESCALE_LOG2) || (mx1 > m1 + RESCALE_LOG2);
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float n0 = fmaxf(m0, mx0), n1 = fmaxf(m1, mx1);
+        const float a0 = (n0 == -INFINITY) ? 1.f : fast_exp2(m0 - n0);
+        const float a1 = (n1 == -INFINITY) ? 1.f : fast_exp2(m1 - n1);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          o0[db] *= a0;
+          o1[db] *= a1;
+        }
+        l0 *= a0;
+        l1 *= a1;
+        m0 = n0;
+        m1 = n1;
+      }
+      const float mb0 = (m0 == -INFINITY) ? 0.f : m0;
+      const float mb1 = (m1 == -INFINITY) ? 0.f : m1;
+      // ---- head 0: P, row sums, PV; head 1's P overlaps head 0's PV MFMAs
+      bf16x8 p0[2], p1[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p0[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(s0[i], c, -mb0));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) l0 = dot2_ones(bf16x2{p0[ks][j], p0[ks][j + 1]}, l0);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) o0[db] = mfma32(va[ks][db], p0[ks], o0[db]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p1[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(s1[i], c, -mb1));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) l1 = dot2_ones(bf16x2{p1[ks][j], p1[ks][j + 1]}, l1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
+#pragma unroll
+      for (int i = 0; i < 2 * DBLK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) o1[db] = mfma32(va[ks][db], p1[ks], o1[db]);
     }
+  };
 
-    wait_vmcnt0();
+  // ---- tile loop, unrolled by NBUF so each buffer index is a constant.  At
+  // tile t: request tile t+2 into the buffer of tile t-1 (every wave finished it
+  // before the barrier closing tile t-1), compute tile t, then publish tile t+1
+  // (its copies were issued one tile earlier; tile t+2's may stay in flight).
+  dma_tile(0, 0);
+  if (ntiles > 1) dma_tile(1, 1);
+  wait_vmcnt0_builtin();   // Q operands and the first two tiles have landed
+  __syncthreads();
+  auto tile = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (t + 2 < ntiles) dma_tile(t + 2, (BUF + 2) % NBUF);
+    if (active) compute_tile(t, bufc);
+    if (t + 2 < ntiles)
+      wait_vmcnt<2 * LOADS>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += NBUF) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < ntiles) tile(t + 2, std::integral_constant<int, 2>{});
   }
 
   if (!active) return;
