@@ -41,7 +41,7 @@ constexpr int BN = 64;           // keys per LDS tile
 constexpr int QB = 32;           // query tokens per wave
 constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
-constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold (log2 domain)
+constexpr float SUM_LIMIT = 65536.0f;  // per-lane half-tile row-sum bound (2^16)
 
 struct Args {
   const bf16* q;
@@ -89,11 +89,11 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   constexpr int DBLK = D / 32;             // PV output d-blocks
   constexpr int LOADS = BN * NCH / THREADS;  // 16-byte chunks per thread per tile (K or V)
   static_assert(LOADS >= 1 && (BN * NCH) % THREADS == 0, "tile/thread mismatch");
-  // K/V tiles triple-buffered: tile t lives in buffer t % NBUF and is requested
-  // two tiles ahead of its use, so its copy overlaps two tiles of compute.  The
-  // NBUF K buffers come first, then the NBUF V buffers, so every operand read is
-  // a per-lane offset plus a compile-time immediate.
-  constexpr int NBUF = 3;
+  // K/V tiles in a 4-deep ring: tile t lives in buffer t % NBUF and is requested
+  // three tiles ahead of its use, so its copy overlaps three tiles of compute.
+  // The NBUF K buffers come first, then the NBUF V buffers, so every operand read
+  // is a per-lane offset plus a compile-time immediate below 64 KB.
+  constexpr int NBUF = 4;
   constexpr int TILE_BYTES = BN * D * 2;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * NBUF * BN * D];
   const char* lds = reinterpret_cast<const char*>(smem);
@@ -243,13 +243,14 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
           va[ks][db] = concat(lds_read_tr4(reinterpret_cast<const bf16*>(vp)),
                               lds_read_tr4(reinterpret_cast<const bf16*>(vp + 8 * D * 2)));
         }
-      // ---- S^T = K Q^T (keys x queries), head 0's MFMAs then head 1's
+      // ---- S^T = K Q^T (keys x queries) for both heads
       const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
       f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) s0 = mfma32(ka[s], qreg[0][s], s0);
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) s1 = mfma32(ka[s], qreg[1][s], s1);
+      for (int s = 0; s < KSTEPS; ++s) {   // two independent accumulation chains
+        s0 = mfma32(ka[s], qreg[0][s], s0);
+        s1 = mfma32(ka[s], qreg[1][s], s1);
+      }
       if (need_mask) {   // causal diagonal and sequence tail
         const int qi = i0 + l32;
 #pragma unroll
@@ -262,51 +263,45 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
           }
         }
       }
-      // ---- online softmax, lazily rescaled
-      float mx0 = max16(s0), mx1 = max16(s1);
-      mx0 = fmaxf(mx0, partner32(mx0, lo)) * c;
-      mx1 = fmaxf(mx1, partner32(mx1, lo)) * c;
-      const bool grow = (mx0 > m0 + RESCALE_LOG2) || (mx1 > m1 + RESCALE_LOG2);
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float n0 = fmaxf(m0, mx0), n1 = fmaxf(m1, mx1);
-        const float a0 = (n0 == -INFINITY) ? 1.f : fast_exp2(m0 - n0);
-        const float a1 = (n1 == -INFINITY) ? 1.f : fast_exp2(m1 - n1);
+      // ---- online softmax per head.  P = exp2(S*c - m) uses the current running
+      // maximum m as is; the half tile's row sums bound every P value (a lane's 16
+      // values are non-negative), so if all sums stay <= 2^16 nothing overflows
+      // and m needs no update.  Otherwise (and on the first half tile, where
+      // m = -inf makes the sums infinite) a rare branch raises m to the true
+      // maximum, rescales O and l, and recomputes P.  Either way numerator and
+      // denominator share one reference, so the result is exact.
+      auto softmax_head = [&](const f32x16& sh, float& m, float& l, bf16x8 (&ph)[2], f32x16 (&oh)[DBLK]) {
+        float lt = 0.f;
+        auto exp_rows = [&](float mb) {
+          lt = 0.f;
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          o0[db] *= a0;
-          o1[db] *= a1;
+          for (int i = 0; i < 16; ++i) ph[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(sh[i], c, -mb));
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) lt = dot2_ones(bf16x2{ph[ks][j], ph[ks][j + 1]}, lt);
+        };
+        exp_rows(m);
+        if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT))) {
+          float mx = max16(sh);
+          mx = fmaxf(mx, partner32(mx, lo)) * c;
+          const float nm = fmaxf(m, mx);
+          const float alpha = (nm == -INFINITY) ? 1.f : fast_exp2(m - nm);
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) oh[db] *= alpha;
+          l *= alpha;
+          m = nm;
+          exp_rows(nm == -INFINITY ? 0.f : nm);
         }
-        l0 *= a0;
-        l1 *= a1;
-        m0 = n0;
-        m1 = n1;
-      }
-      const float mb0 = (m0 == -INFINITY) ? 0.f : m0;
-      const float mb1 = (m1 == -INFINITY) ? 0.f : m1;
-      // ---- head 0: P, row sums, PV; head 1's P overlaps head 0's PV MFMAs
+        l += lt;
+      };
       bf16x8 p0[2], p1[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p0[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(s0[i], c, -mb0));
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) l0 = dot2_ones(bf16x2{p0[ks][j], p0[ks][j + 1]}, l0);
+      softmax_head(s0, m0, l0, p0, o0);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) o0[db] = mfma32(va[ks][db], p0[ks], o0[db]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p1[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(s1[i], c, -mb1));
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) l1 = dot2_ones(bf16x2{p1[ks][j], p1[ks][j + 1]}, l1);
-      __builtin_amdgcn_sched_group_barrier(0x002, 40, 1);
-#pragma unroll
-      for (int i = 0; i < 2 * DBLK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);
-      }
+      softmax_head(s1, m1, l1, p1, o1);   // its VALU work overlaps head 0's PV MFMAs
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -315,18 +310,21 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   };
 
   // ---- tile loop, unrolled by NBUF so each buffer index is a constant.  At
-  // tile t: request tile t+2 into the buffer of tile t-1 (every wave finished it
+  // tile t: request tile t+3 into the buffer of tile t-1 (every wave finished it
   // before the barrier closing tile t-1), compute tile t, then publish tile t+1
-  // (its copies were issued one tile earlier; tile t+2's may stay in flight).
+  // (the copies of tiles t+2 and t+3 may stay in flight).
   dma_tile(0, 0);
   if (ntiles > 1) dma_tile(1, 1);
-  wait_vmcnt0_builtin();   // Q operands and the first two tiles have landed
+  if (ntiles > 2) dma_tile(2, 2);
+  wait_vmcnt0_builtin();   // Q operands and the first tiles have landed
   __syncthreads();
   auto tile = [&](int t, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    if (t + 2 < ntiles) dma_tile(t + 2, (BUF + 2) % NBUF);
+    if (t + 3 < ntiles) dma_tile(t + 3, (BUF + 3) % NBUF);
     if (active) compute_tile(t, bufc);
-    if (t + 2 < ntiles)
+    if (t + 3 < ntiles)
+      wait_vmcnt<4 * LOADS>();
+    else if (t + 2 < ntiles)
       wait_vmcnt<2 * LOADS>();
     else
       wait_vmcnt<0>();
@@ -336,6 +334,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
     tile(t, std::integral_constant<int, 0>{});
     if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
     if (t + 2 < ntiles) tile(t + 2, std::integral_constant<int, 2>{});
+    if (t + 3 < ntiles) tile(t + 3, std::integral_constant<int, 3>{});
   }
 
   if (!active) return;
