@@ -18,7 +18,7 @@
 // partial softmax state (running max m in the log2 domain, denominator l and the
 // unnormalised accumulator) to the workspace.
 //
-// Combine kernel: one workgroup per (b, pair).  For both heads of the pair it
+// Combine kernel: one wave per (b, pair).  For both heads of the pair it
 // merges the partial states (M = max_s m_s, weights 2^(m_s - M)), normalises,
 // forms o_1 - lambda * o_2 (optional V1 RMSNorm) and writes bf16.
 #include "dev_common.h"
@@ -64,10 +64,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
   const int grp = lane >> 4;   // 16-lane group
   const int nq = 2 * a.G;
 
-  const int s = blockIdx.x % a.S;
-  const int bg = blockIdx.x / a.S;
-  const int g = bg % a.Hkv;
-  const int b = bg / a.Hkv;
+  // KV head fastest: the Hkv waves of one (b, key range) are dispatched together
+  // and stream neighbouring 256-byte pieces of the same cache rows.
+  const int g = blockIdx.x % a.Hkv;
+  const int s = (blockIdx.x / a.Hkv) % a.S;
+  const int b = blockIdx.x / (a.Hkv * a.S);
   const int k0 = s * a.chunk;
   const int k1 = min(a.L, k0 + a.chunk);
 
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
       const bool ok = key < k1;
       const bf16* src = kb0 + (size_t)(ok ? key : k0) * row + 8 * grp;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ka[h][ks] = ok ? ldg16(src + 32 * ks) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < KS; ++ks) ka[h][ks] = ok ? ldg16_stream(src + 32 * ks) : u32x4{0, 0, 0, 0};
     }
     u32x4 vr[VLOADS];
 #pragma unroll
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
       const int cid = lane + 64 * j;
       const int r = cid / NCH, ch = cid % NCH;
       const int key = kk + r;
-      vr[j] = key < k1 ? ldg16(vb0 + (size_t)key * row + 8 * ch) : u32x4{0, 0, 0, 0};
+      vr[j] = key < k1 ? ldg16_stream(vb0 + (size_t)key * row + 8 * ch) : u32x4{0, 0, 0, 0};
     }
     // ---- S^T = K Q^T: lane -> query n, keys kk + 16*h + 4*grp + i
     f32x4 s0 = f32x4{}, s1 = f32x4{};
@@ -181,39 +182,63 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
   }
 }
 
+// One wave per (b, pair); lane owns D/64 consecutive output columns.  All
+// partial states of both heads are requested before any is used, so the kernel
+// costs about one memory round trip.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(Args a) {
-  __shared__ float red[D / 64];
+__global__ __launch_bounds__(64) void decode_combine_kernel(Args a) {
+  constexpr int E = D / 64;            // columns per lane
+  constexpr int UNR = 8;               // key ranges in flight per batch of loads
   const int bp = blockIdx.x;
   const int b = bp / a.P, p = bp % a.P;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
   const int rec = D + 4;
-  float o[2];
+  float o[2][E];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const float* base = a.ws + ((size_t)b * a.Hq + 2 * p + h) * a.S * rec;
     float M = -INFINITY;
     for (int s = 0; s < a.S; ++s) M = fmaxf(M, base[s * rec + D]);
-    float acc = 0.f, den = 0.f;
-    for (int s = 0; s < a.S; ++s) {
-      const float ms = base[s * rec + D];
-      const float wgt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-      acc += wgt * base[s * rec + d];
-      den += wgt * base[s * rec + D + 1];
+    float acc[E], den = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += UNR) {
+      float ms[UNR], ls[UNR], av[UNR][E];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int s = min(s0 + u, a.S - 1);
+        ms[u] = base[s * rec + D];
+        ls[u] = base[s * rec + D + 1];
+#pragma unroll
+        for (int e = 0; e < E; ++e) av[u][e] = base[s * rec + E * lane + e];
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const float wgt = (s0 + u >= a.S || ms[u] == -INFINITY) ? 0.f : fast_exp2(ms[u] - M);
+        den += wgt * ls[u];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += wgt * av[u][e];
+      }
     }
-    o[h] = acc / den;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[h][e] = acc[e] / den;
   }
-  float x = o[0] - a.lam[(size_t)b * a.P + p] * o[1];
+  const float lamv = a.lam[(size_t)b * a.P + p];
+  float x[E], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = o[0][e] - lamv * o[1][e];
+    ss += x[e] * x[e];
+  }
   if (a.v1) {
-    float ss = x * x;
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((d & 63) == 0) red[d >> 6] = ss;
-    __syncthreads();
-    ss = 0.f;
-    for (int i = 0; i < D / 64; ++i) ss += red[i];
-    x *= 1.0f / sqrtf(ss / (float)D + a.eps);
+    const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] *= r;
   }
-  a.out[((size_t)b * a.P + p) * D + d] = (bf16)x;
+  bf16* dst = a.out + ((size_t)b * a.P + p) * D + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[e] = (bf16)x[e];
 }
 
 template <int D>
@@ -240,7 +265,7 @@ hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
   hipLaunchKernelGGL(decode_split_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.B * a.P)), dim3(D), 0, st, a);
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.B * a.P)), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -65,6 +65,11 @@ __device__ __forceinline__ float dot2_ones(bf16x2 p, float acc) {
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Streaming 16-byte load (nontemporal hint): data read exactly once, as the
+// decode KV cache is, need not displace reusable lines.
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
 // lds_base + 16*l (lds_base wave-uniform).  Issued as inline asm so the compiler
