@@ -9,26 +9,26 @@
 // GQA group share K/V and the head dim); attention-variants lesson, "步骤1"
 // (causal mask).
 //
-// Work decomposition.  A workgroup of 4 waves owns one (batch b, KV head g)
-// and a block of query tokens.  Each wave owns one differential pair p of that
-// group and 32 query tokens, i.e. 64 query rows (32 tokens x the pair's two
-// heads), so the lambda-subtract happens in registers.  Every K/V tile of 64
+// Work decomposition.  A workgroup of 8 waves (two per SIMD) owns one (batch b,
+// KV head g) and a block of query tokens.  Each wave owns one differential pair
+// p of that group and 16 query tokens: its 32 query rows (16 tokens x the pair's
+// two heads) are the 32 columns of one MFMA tile, column n = 16*head + token, so
+// the lambda-subtract pairs lanes l and l^16 in registers.  Every K/V tile of 64
 // keys is copied from HBM/L2 into LDS once per workgroup and read by all waves:
 // with G = 4 pairs per KV head, one staged byte serves all 8 query heads.  The
 // copy uses the direct global-to-LDS loads (16 bytes per lane, no registers),
-// issued one tile ahead into the other half of a double buffer.
+// issued three tiles ahead into a 4-deep ring.  The two waves of a SIMD
+// interleave: one wave's softmax (VALU) issues while the other's MFMAs run.
 //
-// Per 32-key half-tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// Per 32-key half tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (A = K from LDS, B = Q^T held in registers), so each lane holds the scores of
-// one query against 16 keys; the matching lane l^32 holds the other 16.  Two
-// online-softmax states (one per head of the pair) are kept per query; the
-// running maximum is raised lazily (only when a row's tile maximum exceeds it by
-// more than 2^8), which leaves the result unchanged because numerator and
-// denominator share the stale maximum.  P = exp2(S*log2(e)/sqrt(d) - m) is
-// rounded to bf16 and fed straight from registers as the B operand of
-// O^T += V^T P^T; the V^T operand comes from the row-major V tile via the
-// transposing LDS read.  The epilogue normalises both heads, subtracts
-// lambda * head2 from head1 (optional V1 RMSNorm) and stores bf16.
+// one query row against 16 keys; lane l^32 holds the other 16.  P = exp2(S *
+// log2(e)/sqrt(d) - m) is rounded to bf16 and fed straight from registers as the
+// B operand of O^T += V^T P^T; the V^T operand comes from the row-major V tile
+// via the transposing LDS read.  The running maximum m is raised only when a
+// half tile's row sums could overflow (see the softmax step below).  The
+// epilogue normalises each row, subtracts lambda * head 1 from head 0 of the
+// same token, applies the optional V1 RMSNorm and stores bf16.
 #include <type_traits>
 
 #include "dev_common.h"
@@ -38,8 +38,8 @@ namespace diffattn {
 namespace {
 
 constexpr int BN = 64;           // keys per LDS tile
-constexpr int QB = 32;           // query tokens per wave
-constexpr int WAVES = 4;
+constexpr int QT = 16;           // query tokens per wave (x 2 heads = 32 MFMA columns)
+constexpr int WAVES = 8;
 constexpr int THREADS = 64 * WAVES;
 constexpr float SUM_LIMIT = 65536.0f;  // per-lane half-tile row-sum bound (2^16)
 
@@ -53,7 +53,7 @@ struct Args {
   int causal, v1;
   float eps, scale_log2;
   int ppw;     // pairs per workgroup
-  int nsub;    // 32-token sub-blocks per workgroup
+  int nsub;    // 16-token sub-blocks per workgroup
   int chunks;  // workgroups needed to cover the G pairs of one KV head
   int ntb;     // token blocks
   int units;   // B * Hkv * chunks
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   // masking decisions) stays wave-uniform and compiles to scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool lo = lane < 32;
-  const int l32 = lane & 31;
+  const int l32 = lane & 31;   // MFMA column: query row 16*head + token
 
   // ---- workgroup -> (token block, b, g, pair chunk).  Token blocks run longest
   // first (causal work grows with the block index); when the (b, g, chunk) units
@@ -127,44 +127,39 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   const int bg = u / a.chunks;
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
-  const int tokens_wg = QB * a.nsub;
+  const int tokens_wg = QT * a.nsub;
   const int tok0 = tb * tokens_wg;
   const int sub = wave / a.ppw;
   const int pig = chunk * a.ppw + (wave % a.ppw);
   const bool active = sub < a.nsub && pig < a.G;
   const int p = g * a.G + pig;
-  const int i0 = tok0 + sub * QB;          // first query token of this wave
+  const int i0 = tok0 + sub * QT;          // first query token of this wave
   const int T = a.T;
+  const int qtok = i0 + (l32 & 15);        // this lane's query token
+  const int qhead = l32 >> 4;              // 0: positive branch, 1: subtracted branch
 
   const int kv_end = a.causal ? min(T, tok0 + tokens_wg) : T;
   const int ntiles = (kv_end + BN - 1) / BN;
-  const size_t kv_row = (size_t)a.Hkv * D;                       // elements between keys
   const bf16* kbase = a.k + ((size_t)b * T * a.Hkv + g) * D;
   const bf16* vbase = a.v + ((size_t)b * T * a.Hkv + g) * D;
 
-  // ---- Q^T operand in registers: lane -> query token i0 + l32, d = 16*s + 8*(lane/32) + 0..7
-  bf16x8 qreg[2][KSTEPS];
+  // ---- Q^T operand in registers: lane -> query row l32, d = 16*s + 8*(lane/32) + 0..7
+  bf16x8 qreg[KSTEPS];
   {
-    const int qi = i0 + l32;
-    const bool ok = active && qi < T;
-    for (int h = 0; h < 2; ++h) {
-      const bf16* src = a.q + (((size_t)b * T + (ok ? qi : 0)) * a.Hq + 2 * p + h) * D + 8 * (lane >> 5);
+    const bool ok = active && qtok < T;
+    const bf16* src = a.q + (((size_t)b * T + (ok ? qtok : 0)) * a.Hq + 2 * p + qhead) * D + 8 * (lane >> 5);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        u32x4 x = ok ? ldg16(src + 16 * s) : u32x4{0, 0, 0, 0};
-        qreg[h][s] = __builtin_bit_cast(bf16x8, x);
-      }
+    for (int s = 0; s < KSTEPS; ++s) {
+      u32x4 x = ok ? ldg16(src + 16 * s) : u32x4{0, 0, 0, 0};
+      qreg[s] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  f32x16 o0[DBLK], o1[DBLK];
+  f32x16 o[DBLK];
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) {
-    o0[i] = f32x16{};
-    o1[i] = f32x16{};
-  }
-  float m0 = -INFINITY, m1 = -INFINITY;   // running maxima (log2 domain), uniform over l, l^32
-  float l0 = 0.f, l1 = 0.f;               // this lane's share of the softmax denominators
+  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
+  float m = -INFINITY;   // running maximum (log2 domain), uniform over lanes l, l^32
+  float l = 0.f;         // this lane's share of the softmax denominator
   const float c = a.scale_log2;
 
   // ---- direct global -> LDS tile copy.  Wave-instruction j of wave w fills the
@@ -221,13 +216,24 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   // (v_phys of row vrow + 16*ks + 8*r + 32*kb equals v_phys(vrow) + that many rows:
   // the V swizzle depends on row % 4 only.)
 
+  // P = exp2(S*c - mb) as the bf16 B operand, and this lane's share of its row sum
+  auto exp_rows = [&](const f32x16& sh, float mb, bf16x8 (&ph)[2], float& lt) {
+    lt = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ph[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(sh[i], c, -mb));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) lt = dot2_ones(bf16x2{ph[ks][j], ph[ks][j + 1]}, lt);
+  };
+
   auto compute_tile = [&](int t, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int kbase_tok = t * BN + kb * 32;
       if (kbase_tok >= T) break;
-      if (a.causal && kbase_tok > i0 + QB - 1) break;
+      if (a.causal && kbase_tok > i0 + QT - 1) break;
 
       // ---- K operands and V^T operands of this half tile
       bf16x8 ka[KSTEPS];
@@ -243,69 +249,50 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
           va[ks][db] = concat(lds_read_tr4(reinterpret_cast<const bf16*>(vp)),
                               lds_read_tr4(reinterpret_cast<const bf16*>(vp + 8 * D * 2)));
         }
-      // ---- S^T = K Q^T (keys x queries) for both heads
-      const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+      // ---- S^T = K Q^T (keys x query rows), two independent accumulation chains
+      f32x16 sa = f32x16{}, sb = f32x16{};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {   // two independent accumulation chains
-        s0 = mfma32(ka[s], qreg[0][s], s0);
-        s1 = mfma32(ka[s], qreg[1][s], s1);
+      for (int s = 0; s < KSTEPS; s += 2) {
+        sa = mfma32(ka[s], qreg[s], sa);
+        sb = mfma32(ka[s + 1], qreg[s + 1], sb);
       }
+      f32x16 sc = sa + sb;
+      const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
       if (need_mask) {   // causal diagonal and sequence tail
-        const int qi = i0 + l32;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          const bool vis = key < T && (!a.causal || key <= qi);
-          if (!vis) {
-            s0[i] = -INFINITY;
-            s1[i] = -INFINITY;
-          }
+          const bool vis = key < T && (!a.causal || key <= qtok);
+          if (!vis) sc[i] = -INFINITY;
         }
       }
-      // ---- online softmax per head.  P = exp2(S*c - m) uses the current running
-      // maximum m as is; the half tile's row sums bound every P value (a lane's 16
-      // values are non-negative), so if all sums stay <= 2^16 nothing overflows
-      // and m needs no update.  Otherwise (and on the first half tile, where
-      // m = -inf makes the sums infinite) a rare branch raises m to the true
-      // maximum, rescales O and l, and recomputes P.  Either way numerator and
-      // denominator share one reference, so the result is exact.
-      auto softmax_head = [&](const f32x16& sh, float& m, float& l, bf16x8 (&ph)[2], f32x16 (&oh)[DBLK]) {
-        float lt = 0.f;
-        auto exp_rows = [&](float mb) {
-          lt = 0.f;
+      // ---- online softmax.  P = exp2(S*c - m) uses the current running maximum
+      // m as is; the half tile's row sums bound every P value (a lane's 16 values
+      // are non-negative), so if all sums stay <= 2^16 nothing overflows and m
+      // needs no update.  Otherwise (and on the first half tile, where m = -inf
+      // makes the sums infinite) a rare branch raises m to the true maximum,
+      // rescales O and l, and recomputes P.  Either way numerator and denominator
+      // share one reference, so the result is exact.
+      bf16x8 pp[2];
+      float lt;
+      exp_rows(sc, m, pp, lt);
+      if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT))) {
+        float mx = max16(sc);
+        mx = fmaxf(mx, partner32(mx, lo)) * c;
+        const float nm = fmaxf(m, mx);
+        const float alpha = (nm == -INFINITY) ? 1.f : fast_exp2(m - nm);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) ph[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(sh[i], c, -mb));
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) lt = dot2_ones(bf16x2{ph[ks][j], ph[ks][j + 1]}, lt);
-        };
-        exp_rows(m);
-        if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT))) {
-          float mx = max16(sh);
-          mx = fmaxf(mx, partner32(mx, lo)) * c;
-          const float nm = fmaxf(m, mx);
-          const float alpha = (nm == -INFINITY) ? 1.f : fast_exp2(m - nm);
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) oh[db] *= alpha;
-          l *= alpha;
-          m = nm;
-          exp_rows(nm == -INFINITY ? 0.f : nm);
-        }
-        l += lt;
-      };
-      bf16x8 p0[2], p1[2];
-      softmax_head(s0, m0, l0, p0, o0);
+        for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+        l *= alpha;
+        m = nm;
+        exp_rows(sc, nm == -INFINITY ? 0.f : nm, pp, lt);
+      }
+      l += lt;
+      // ---- O^T += V^T P^T
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) o0[db] = mfma32(va[ks][db], p0[ks], o0[db]);
-      softmax_head(s1, m1, l1, p1, o1);   // its VALU work overlaps head 0's PV MFMAs
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) o1[db] = mfma32(va[ks][db], p1[ks], o1[db]);
+        for (int db = 0; db < DBLK; ++db) o[db] = mfma32(va[ks][db], pp[ks], o[db]);
     }
   };
 
@@ -338,14 +325,12 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   }
 
   if (!active) return;
-  // ---- epilogue: normalise, subtract lambda * head 2, optional RMSNorm, store
-  l0 += partner32(l0, lo);
-  l1 += partner32(l1, lo);
-  const int qi = i0 + l32;
-  const bool ok = qi < T;
-  const float lamv = ok ? a.lam[((size_t)b * T + qi) * a.P + p] : 0.f;
-  const float inv0 = 1.0f / l0;
-  const float inv1 = lamv / l1;
+  // ---- epilogue: normalise each row, subtract lambda * head 1 (columns 16-31,
+  // lanes l^16) from head 0 (columns 0-15), optional RMSNorm, store head-0 lanes
+  l += partner32(l, lo);
+  const bool ok = qhead == 0 && qtok < T;
+  const float lamv = ok ? a.lam[((size_t)b * T + qtok) * a.P + p] : 0.f;
+  const float inv = 1.0f / l;
   float ss = 0.f;
   {
     // Both products are rounded before the subtraction (FMA contraction off), so
@@ -356,8 +341,10 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float x = o0[db][i] * inv0 - o1[db][i] * inv1;
-        o0[db][i] = x;
+        const float y = o[db][i] * inv;
+        const float y1 = __shfl_xor(y, 16);
+        const float x = y - lamv * y1;
+        o[db][i] = x;
         ss += x * x;
       }
     }
@@ -366,17 +353,17 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
     ss += partner32(ss, lo);
     const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) o0[db] *= r;
+    for (int db = 0; db < DBLK; ++db) o[db] *= r;
   }
   if (!ok) return;
-  bf16* dst = a.out + (((size_t)b * T + qi) * a.P + p) * D + 4 * (lane >> 5);
+  bf16* dst = a.out + (((size_t)b * T + qtok) * a.P + p) * D + 4 * (lane >> 5);
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (bf16)o0[db][4 * i4 + e];
+      for (int e = 0; e < 4; ++e) w[e] = (bf16)o[db][4 * i4 + e];
       *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * i4) = w;
     }
   }
@@ -403,7 +390,7 @@ hipError_t launch(const PrefillProblem& pr, hipStream_t s) {
   a.ppw = a.G < WAVES ? a.G : WAVES;
   a.nsub = WAVES / a.ppw;
   a.chunks = (a.G + a.ppw - 1) / a.ppw;
-  const int tokens_wg = QB * a.nsub;
+  const int tokens_wg = QT * a.nsub;
   a.ntb = (a.T + tokens_wg - 1) / tokens_wg;
   a.units = a.B * a.Hkv * a.chunks;
   const long long blocks = (long long)a.ntb * a.units;
