@@ -9,7 +9,11 @@ decode launches are each bracketed by HIP events on the stream they run on;
 query-key-head, causal) over its mean launch time, and the decode's KV-cache
 GB/s (every K/V byte once) is reported beside it.  Rank 0 prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--settle-ms 300] [--no-cpu-baseline]
+
+Before the warmup steps the path runs for --settle-ms of wall time: MI355X's
+clock ramps from about 1.9 to 2.35 GHz over the first tens of ms of sustained
+load, and the timed steps are meant to see the sustained clock.
 """
 from __future__ import annotations
 
@@ -61,9 +65,10 @@ def cpu_baseline(budget_s: float) -> dict:
     inp = W.make_prefill(w)
     q, k, v = (W.to_f64(inp[n], "bf16") for n in ("q", "k", "v"))
     G = w.G
+    # whole pairs (all rows, both heads), cycling over the P pairs until the budget is spent
     done, t0 = 0, time.perf_counter()
-    while done < w.P and time.perf_counter() - t0 < budget_s:
-        p = done
+    while time.perf_counter() - t0 < budget_s:
+        p = done % w.P
         g = p // G
         oracle.diffattn_prefill(q[:, :, 2 * p:2 * p + 2], k[:, :, g:g + 1], v[:, :, g:g + 1],
                                 inp["lam"][:, :, p:p + 1])
@@ -71,15 +76,17 @@ def cpu_baseline(budget_s: float) -> dict:
     dt = time.perf_counter() - t0
     flops = w.prefill_flops() * done / w.P
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads or 1), "kind": "oracle",
-            "sample": f"c2 prefill, {done} of {w.P} pairs x all {w.T} rows, fp64 numpy (OpenBLAS), {dt:.1f} s"}
+            "sample": f"c2 prefill, {done} pair passes ({w.P} pairs in the workload) x all {w.T} rows, "
+                      f"fp64 numpy (OpenBLAS), {dt:.1f} s"}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed steps; the GPU clock needs tens of ms of load to ramp up")
+    ap.add_argument("--warmup", type=int, default=50, help="untimed steps after the clock settle phase")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed wall time of steps before the warmup steps (clock ramp-up); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
@@ -143,6 +150,11 @@ def main() -> int:
             bd.decode(dq, dk, dv, dlam, workspace=dws, out=dout)
             if evs: evs[3].record(stream)
 
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

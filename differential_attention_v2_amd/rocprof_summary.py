@@ -45,6 +45,19 @@ def cmd_stats(a) -> None:
     for r in rows:
         lines.append(f"{_short(r['Name'])[:48]:48s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
                      f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} {float(r['Percentage']):7.2f}")
+    if a.trace:
+        # the last N dispatches of each kernel: the steps that bench.py times
+        per = {}
+        for r in csv.DictReader(open(a.trace)):
+            per.setdefault(_short(r["Kernel_Name"]), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        lines += ["", f"last {a.last} dispatches of each kernel (the timed steps):",
+                  f"{'kernel':48s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+        for k, v in per.items():
+            if len(v) < a.last:
+                continue
+            d = [x[1] / 1e3 for x in sorted(v)[-a.last:]]
+            lines.append(f"{k[:48]:48s} {len(d):6d} {statistics.mean(d):10.2f} {min(d):10.2f} {max(d):10.2f}")
     if a.note:
         lines += ["", a.note]
     open(a.out, "w").write("\n".join(lines) + "\n")
@@ -107,6 +120,8 @@ def main(argv=None) -> int:
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--note", default="")
+    s.add_argument("--trace", default=None, help="run_kernel_trace.csv, for the mean of the last dispatches")
+    s.add_argument("--last", type=int, default=20)
     s.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     for n in ("fetch", "write", "copy_fetch", "copy_write"):
