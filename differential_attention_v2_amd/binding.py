@@ -31,6 +31,10 @@ _SIGNATURES = {
                                       _c_int, _c_uint, _c_float, _vp]),
     "diffattn_decode_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, _c_uint, _c_float, _c_int, _vp, _c_size, _vp]),
+    "diffattn_prefill_fwd_train": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_int, _vp]),
+    "diffattn_prefill_bwd": (_c_int, [_vp] * 12 + [_c_int] * 6 + [_vp, _c_size, _vp]),
+    "diffattn_prefill_bwd_workspace_bytes": (_c_size, [_c_int] * 5),
     "diffattn_decode_num_splits": (_c_int, [_c_int] * 5),
     "diffattn_decode_workspace_bytes": (_c_size, [_c_int] * 6),
     "diffattn_v1_lambda": (_c_int, [_vp, _vp, _vp, _vp, _c_float, _vp, _c_int, _c_int, _c_int, _vp]),
@@ -73,6 +77,20 @@ def diffattn_decode_fwd(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, 
                         workspace, workspace_bytes, stream):
     return load_library().diffattn_decode_fwd(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, flags,
                                               rms_eps, num_splits, workspace, workspace_bytes, stream)
+
+
+def diffattn_prefill_fwd_train(q, k, v, lam, out, o2, lse, B, T, Hq, Hkv, d, causal, stream):
+    return load_library().diffattn_prefill_fwd_train(q, k, v, lam, out, o2, lse, B, T, Hq, Hkv, d, causal, stream)
+
+
+def diffattn_prefill_bwd(q, k, v, lam, out, o2, lse, dout, dq, dk, dv, dlam, B, T, Hq, Hkv, d, causal,
+                         workspace, workspace_bytes, stream):
+    return load_library().diffattn_prefill_bwd(q, k, v, lam, out, o2, lse, dout, dq, dk, dv, dlam, B, T, Hq, Hkv,
+                                               d, causal, workspace, workspace_bytes, stream)
+
+
+def diffattn_prefill_bwd_workspace_bytes(B, T, Hq, Hkv, d):
+    return load_library().diffattn_prefill_bwd_workspace_bytes(B, T, Hq, Hkv, d)
 
 
 def diffattn_decode_num_splits(B, L, Hq, Hkv, d):
@@ -151,6 +169,57 @@ def prefill(q, k, v, lam, causal: bool = True, v1_rmsnorm: bool = False, eps: fl
     if st != DIFFATTN_OK:
         raise DiffAttnError(st, "diffattn_prefill_fwd")
     return out
+
+
+def prefill_train(q, k, v, lam, causal: bool = True, stream=None):
+    """(out, o2, lse) of the bf16 training forward: out [B,T,P,d], o2 [B,T,P,d], lse [B,T,Hq] fp32."""
+    torch = _torch()
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    _check(q, "q", (B, T, Hq, d), torch.bfloat16)
+    _check(k, "k", (B, T, Hkv, d), torch.bfloat16)
+    _check(v, "v", (B, T, Hkv, d), torch.bfloat16)
+    _check(lam, "lam", (B, T, Hq // 2), torch.float32)
+    out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device)
+    o2 = torch.empty_like(out)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    st = diffattn_prefill_fwd_train(q.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(), out.data_ptr(),
+                                    o2.data_ptr(), lse.data_ptr(), B, T, Hq, Hkv, d, int(bool(causal)),
+                                    _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_prefill_fwd_train")
+    return out, o2, lse
+
+
+def prefill_backward(q, k, v, lam, out, o2, lse, dout, causal: bool = True, workspace=None, grads=None,
+                     stream=None):
+    """(dq, dk, dv, dlam) of L = sum(dout * out) for the bf16 prefill map."""
+    torch = _torch()
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    P = Hq // 2
+    _check(q, "q", (B, T, Hq, d), torch.bfloat16)
+    _check(k, "k", (B, T, Hkv, d), torch.bfloat16)
+    _check(v, "v", (B, T, Hkv, d), torch.bfloat16)
+    _check(lam, "lam", (B, T, P), torch.float32)
+    for name, t in (("out", out), ("o2", o2), ("dout", dout)):
+        _check(t, name, (B, T, P, d), torch.bfloat16)
+    _check(lse, "lse", (B, T, Hq), torch.float32)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(lam))
+    dq, dk, dv, dlam = grads
+    if workspace is None:
+        n = diffattn_prefill_bwd_workspace_bytes(B, T, Hq, Hkv, d)
+        if n == 0:
+            raise ValueError("invalid backward sizes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    st = diffattn_prefill_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(), out.data_ptr(),
+                              o2.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), dlam.data_ptr(), B, T, Hq, Hkv, d, int(bool(causal)),
+                              workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_prefill_bwd")
+    return dq, dk, dv, dlam
 
 
 def decode_workspace(B, L, Hq, Hkv, d, num_splits: int = 0, device="cuda"):

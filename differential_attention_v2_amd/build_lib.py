@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip", "backward_bf16.hip"]
 
 # Packed-fp32 VALU instructions are kept out of every kernel; hipcc -O3 would
 # otherwise form them from plain float code.

@@ -85,6 +85,46 @@ int diffattn_prefill_fwd(const void* q, const void* k, const void* v, const floa
   return hip_status(launch_prefill_bf16(p, s));
 }
 
+int diffattn_prefill_fwd_train(const void* q, const void* k, const void* v, const float* lambda, void* out,
+                               void* o2, float* lse, int B, int T, int Hq, int Hkv, int d, int causal,
+                               void* stream) {
+  if (B < 1 || T < 1) return DIFFATTN_ERR_INVALID_ARG;
+  int st = check_heads(Hq, Hkv, d);
+  if (st) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(o2, 16) ||
+      !aligned(lambda, 4) || !aligned(lse, 4))
+    return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(B, T, Hq, d) || (long long)B * T * (Hq / 2) > kMaxGrid) return DIFFATTN_ERR_INVALID_ARG;
+  PrefillProblem p{q, k, v, lambda, out, B, T, Hq, Hkv, d, causal ? 1 : 0, 0, 0.f};
+  p.o2 = o2;
+  p.lse = lse;
+  return hip_status(launch_prefill_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t diffattn_prefill_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
+  if (B < 1 || T < 1 || check_heads(Hq, Hkv, d) != DIFFATTN_OK || !fits(B, T, Hq, d)) return 0;
+  return backward_workspace_floats(B, T, Hq, Hkv, d) * sizeof(float);
+}
+
+int diffattn_prefill_bwd(const void* q, const void* k, const void* v, const float* lambda, const void* out,
+                         const void* o2, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         float* dlambda, int B, int T, int Hq, int Hkv, int d, int causal, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (B < 1 || T < 1) return DIFFATTN_ERR_INVALID_ARG;
+  int st = check_heads(Hq, Hkv, d);
+  if (st) return st;
+  for (const void* p16 : {q, k, v, out, o2, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv)})
+    if (!aligned(p16, 16)) return DIFFATTN_ERR_INVALID_ARG;
+  if (!aligned(lambda, 4) || !aligned(lse, 4) || !aligned(dlambda, 4)) return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(B, T, Hq, d) || (long long)B * T * (Hq / 2) > kMaxGrid) return DIFFATTN_ERR_INVALID_ARG;
+  const size_t need = backward_workspace_floats(B, T, Hq, Hkv, d) * sizeof(float);
+  if (!aligned(workspace, 16) || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+  BackwardProblem p{q, k, v, lambda, out, o2, lse, dout, dq, dk, dv, dlambda, static_cast<float*>(workspace),
+                    B, T, Hq, Hkv, d, causal ? 1 : 0};
+  return hip_status(launch_backward_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
 int diffattn_decode_num_splits(int B, int L, int Hq, int Hkv, int d) {
   if (check_heads(Hq, Hkv, d) != DIFFATTN_OK) return 0;
   int S, chunk;

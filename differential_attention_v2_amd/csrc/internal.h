@@ -15,6 +15,10 @@ struct PrefillProblem {
   int causal;
   int v1_rmsnorm;
   float eps;
+  // training forward only (bf16, V2): the subtracted branch's output [B, T, P, d]
+  // and the natural-log log-sum-exp of every row [B, T, Hq]; null otherwise
+  void* o2 = nullptr;
+  float* lse = nullptr;
 };
 
 struct DecodeProblem {
@@ -31,12 +35,43 @@ struct DecodeProblem {
   float eps;
 };
 
+// Backward pass (bf16, V2).  The workspace holds, in order: per-pair row
+// statistics [B][P][5][Tpad] fp32 (log2-domain LSE of both heads, D_1, D_2,
+// lambda; Tpad = T rounded up to 32), then fp32 dK and dV accumulators
+// [B, T, Hkv, d] each.
+struct BackwardProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* lam;
+  const void* out;
+  const void* o2;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dlam;
+  float* ws;
+  int B, T, Hq, Hkv, d;
+  int causal;
+};
+constexpr int kBackwardFields = 5;
+inline int backward_tpad(int T) { return (T + 31) / 32 * 32; }
+inline size_t backward_rs_floats(int B, int T, int Hq) {
+  return (size_t)B * (Hq / 2) * kBackwardFields * backward_tpad(T);
+}
+inline size_t backward_workspace_floats(int B, int T, int Hq, int Hkv, int d) {
+  return backward_rs_floats(B, T, Hq) + 2 * (size_t)B * T * Hkv * d;
+}
+
 // Floats per partial-state record in the decode workspace: acc[d], m, l, 2 pad
 // (keeps every record 16-byte aligned).
 inline int decode_record_floats(int d) { return d + 4; }
 
 hipError_t launch_prefill_bf16(const PrefillProblem& p, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeProblem& p, hipStream_t s);
+hipError_t launch_backward_bf16(const BackwardProblem& p, hipStream_t s);
 // fp32 path: rows of queries [B, Tq] over Tk keys; causal limit j <= i + (Tk - Tq).
 hipError_t launch_rows_f32(const PrefillProblem& p, int Tq, int Tk, hipStream_t s);
 hipError_t launch_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,

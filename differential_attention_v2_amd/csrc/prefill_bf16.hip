@@ -49,6 +49,8 @@ struct Args {
   const bf16* v;
   const float* lam;
   bf16* out;
+  bf16* o2;     // training forward: A_2 V per pair, or null
+  float* lse;   // training forward: log-sum-exp per query row and head, or null
   int B, T, Hq, Hkv, G, P;
   int causal, v1;
   float eps, scale_log2;
@@ -328,6 +330,8 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   // ---- epilogue: normalise each row, subtract lambda * head 1 (columns 16-31,
   // lanes l^16) from head 0 (columns 0-15), optional RMSNorm, store head-0 lanes
   l += partner32(l, lo);
+  if (a.lse != nullptr && lo && qtok < T)   // natural-log LSE of the row's scaled scores
+    a.lse[((size_t)b * T + qtok) * a.Hq + 2 * p + qhead] = (m + __log2f(l)) * 0.6931471805599453f;
   const bool ok = qhead == 0 && qtok < T;
   const float lamv = ok ? a.lam[((size_t)b * T + qtok) * a.P + p] : 0.f;
   const float inv = 1.0f / l;
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   {
     // Both products are rounded before the subtraction (FMA contraction off), so
     // the two branches are treated alike and identical branches with lambda = 1
-    // cancel exactly.
+    // cancel exactly.  Head-1 lanes keep their own normalised row (A_2 V).
 #pragma clang fp contract(off)
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
@@ -343,30 +347,33 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
       for (int i = 0; i < 16; ++i) {
         const float y = o[db][i] * inv;
         const float y1 = __shfl_xor(y, 16);
-        const float x = y - lamv * y1;
+        const float x = qhead == 0 ? y - lamv * y1 : y;
         o[db][i] = x;
         ss += x * x;
       }
     }
   }
+  auto store_rows = [&](bf16* base) {
+    bf16* dst = base + (((size_t)b * T + qtok) * a.P + p) * D + 4 * (lane >> 5);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)o[db][4 * i4 + e];
+        *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * i4) = w;
+      }
+    }
+  };
+  if (a.o2 != nullptr && qhead == 1 && qtok < T) store_rows(a.o2);
   if (a.v1) {
     ss += partner32(ss, lo);
     const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) o[db] *= r;
   }
-  if (!ok) return;
-  bf16* dst = a.out + (((size_t)b * T + qtok) * a.P + p) * D + 4 * (lane >> 5);
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db) {
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (bf16)o[db][4 * i4 + e];
-      *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * i4) = w;
-    }
-  }
+  if (ok) store_rows(a.out);
 }
 
 template <int D>
@@ -377,6 +384,8 @@ hipError_t launch(const PrefillProblem& pr, hipStream_t s) {
   a.v = static_cast<const bf16*>(pr.v);
   a.lam = pr.lam;
   a.out = static_cast<bf16*>(pr.out);
+  a.o2 = static_cast<bf16*>(pr.o2);
+  a.lse = pr.lse;
   a.B = pr.B;
   a.T = pr.T;
   a.Hq = pr.Hq;

@@ -128,6 +128,12 @@ class Workload:
         pairs = T * (T + 1) / 2 if self.causal else T * T
         return 4.0 * self.d * self.Hq * self.B * pairs
 
+    def prefill_bwd_flops(self) -> float:
+        """8*d flops per visible (query, key, head): the four gradient products
+        dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q (2*d each), without the
+        score recomputation."""
+        return 2.0 * self.prefill_flops()
+
     def decode_kv_bytes(self) -> float:
         """K and V cache bytes, each byte counted once per KV-head group."""
         esize = 2 if self.dtype == "bf16" else 4
@@ -162,6 +168,14 @@ def make_prefill(w: Workload) -> dict:
     v = _normal(s[_S_V], w.B * w.T * w.Hkv * w.d, w.qkv_scale, w.dtype).reshape(w.B, w.T, w.Hkv, w.d)
     z = _normal(s[_S_LAM], w.B * w.T * w.P, 1.0, "fp32").reshape(w.B, w.T, w.P)
     return dict(q=q, k=k, v=v, lam=_sigmoid_f32(z))
+
+
+def make_dout(w: Workload) -> np.ndarray:
+    """Output gradient for the backward pass: N(0, 1) in the workload's dtype, [B, T, P, d],
+    from a stream independent of the forward inputs."""
+    assert w.kind == "prefill"
+    s = np.random.SeedSequence([w.seed, 7])
+    return _normal(s, w.B * w.T * w.P * w.d, 1.0, w.dtype).reshape(w.B, w.T, w.P, w.d)
 
 
 def make_decode(w: Workload) -> dict:

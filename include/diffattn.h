@@ -74,6 +74,46 @@ int diffattn_prefill_fwd(const void* q, const void* k, const void* v, const floa
                          int dtype, unsigned flags, float rms_eps, void* stream);
 
 /*
+ * Training forward (bf16, V2 map, no RMSNorm): the prefill above, plus what the
+ * backward needs -- the subtracted branch's output and each row's log-sum-exp.
+ *   q, k, v, lambda, out, causal   as diffattn_prefill_fwd (bf16 only)
+ *   o2     device [B, T, P, d] bf16: A_2 V for every pair (head 2p+1's attention
+ *          output before lambda), fully overwritten
+ *   lse    device [B, T, Hq] fp32: log sum_j exp(q_h . k_j / sqrt(d)) over the
+ *          visible keys of each row and query head (natural log)
+ * Returns a diffattn_status_t.
+ */
+int diffattn_prefill_fwd_train(const void* q, const void* k, const void* v, const float* lambda, void* out,
+                               void* o2, float* lse, int B, int T, int Hq, int Hkv, int d, int causal,
+                               void* stream);
+
+/*
+ * Backward of the prefill map for training (the pages report pretraining
+ * results and motivate V2 by training stability: dailytechsnack.ch article,
+ * section "Weniger Ausreisser und Gradientenspitzen").  Gradients of
+ * L = sum(dout * out) with out = A_1 V - lambda A_2 V (differential-attention
+ * lesson "差异性注意力 (V2)", section "差异性概念"), bf16 V2 map only.
+ *   q, k, v, lambda, causal   the forward's inputs
+ *   out, o2, lse              the training forward's outputs for those inputs
+ *   dout   device [B, T, P, d] bf16
+ *   dq     device [B, T, Hq, d] bf16 (out)      dk, dv  device [B, T, Hkv, d] bf16 (out)
+ *   dlambda device [B, T, P] fp32 (out)
+ *   workspace  device scratch >= diffattn_prefill_bwd_workspace_bytes(...) bytes,
+ *              16-byte aligned; contents on entry are ignored
+ * Outputs are fully overwritten and must not alias any input.  dk and dv are
+ * summed over query chunks with fp32 atomics, so their last bits can vary from
+ * run to run; dq and dlambda are deterministic.
+ * Returns a diffattn_status_t.
+ */
+int diffattn_prefill_bwd(const void* q, const void* k, const void* v, const float* lambda, const void* out,
+                         const void* o2, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         float* dlambda, int B, int T, int Hq, int Hkv, int d, int causal, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Workspace bytes diffattn_prefill_bwd needs (host only; 0 on invalid sizes). */
+size_t diffattn_prefill_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
+
+/*
  * Decode: one new query token per sequence against a contiguous KV cache that
  * already holds that token (the query sits at position L-1 and sees all L rows).
  * Each cache byte is read from HBM once per KV-head group (both heads of every

@@ -140,3 +140,53 @@ def test_product_path_does_not_import_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
                 assert "diffattn_oracle" not in text, f
+
+
+def _train(**kw):
+    a = dict(q=P, k=P, v=P, lam=P, out=P, o2=P, lse=P, B=1, T=16, Hq=8, Hkv=2, d=128, causal=1, stream=None)
+    a.update(kw)
+    return bd.diffattn_prefill_fwd_train(**a)
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, lam=P, out=P, o2=P, lse=P, dout=P, dq=P, dk=P, dv=P, dlam=P, B=1, T=16, Hq=8, Hkv=2,
+             d=128, causal=1, workspace=P, workspace_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return bd.diffattn_prefill_bwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o2=None), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(lse=None), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(o2=P + 8), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(lse=P + 2), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(T=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(d=96), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=2), bd.DIFFATTN_ERR_INVALID_ARG),
+])
+def test_train_forward_rejects(lib, kw, status):
+    assert _train(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=None), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(dq=P + 8), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(dlam=None), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(lse=P + 1), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(B=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(d=32), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(Hq=36, Hkv=2), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(workspace=None), bd.DIFFATTN_ERR_WORKSPACE),
+    (dict(workspace_bytes=1024), bd.DIFFATTN_ERR_WORKSPACE),
+    (dict(workspace=P + 4), bd.DIFFATTN_ERR_WORKSPACE),
+])
+def test_backward_rejects(lib, kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_backward_workspace_bytes(lib):
+    # per-pair row statistics [B][P][5][T rounded up to 32] + fp32 dK and dV accumulators
+    assert bd.diffattn_prefill_bwd_workspace_bytes(1, 4096, 64, 8, 128) == (32 * 5 * 4096 + 2 * 4096 * 8 * 128) * 4
+    assert bd.diffattn_prefill_bwd_workspace_bytes(2, 100, 8, 2, 64) == (2 * 4 * 5 * 128 + 2 * 2 * 100 * 2 * 64) * 4
+    assert bd.diffattn_prefill_bwd_workspace_bytes(1, 100, 6, 2, 64) == 0
+    assert bd.diffattn_prefill_bwd_workspace_bytes(0, 100, 8, 2, 64) == 0
