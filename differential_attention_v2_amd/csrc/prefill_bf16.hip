@@ -229,95 +229,100 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
       for (int j = 0; j < 8; j += 2) lt = dot2_ones(bf16x2{ph[ks][j], ph[ks][j + 1]}, lt);
   };
 
-  auto compute_tile = [&](int t, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
+  // Last 32-key half tile this wave reads; K operands are read one half tile
+  // ahead into ka, right after the S products of the current one have issued.
+  const int hl = active ? ((a.causal ? min(T, i0 + QT) : T) + 31) / 32 - 1 : -1;
+  bf16x8 ka[KSTEPS];
+  auto load_k = [&](int off) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kbase_tok = t * BN + kb * 32;
-      if (kbase_tok >= T) break;
-      if (a.causal && kbase_tok > i0 + QT - 1) break;
-
-      // ---- K operands and V^T operands of this half tile
-      bf16x8 ka[KSTEPS];
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        ka[s] = *reinterpret_cast<const bf16x8*>(lds + kofs[s] + BUF * TILE_BYTES + kb * 32 * D * 2);
-      bf16x8 va[2][DBLK];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const char* vp = lds + vofs[db] + BUF * TILE_BYTES + (kb * 32 + 16 * ks) * D * 2;
-          va[ks][db] = concat(lds_read_tr4(reinterpret_cast<const bf16*>(vp)),
-                              lds_read_tr4(reinterpret_cast<const bf16*>(vp + 8 * D * 2)));
-        }
-      // ---- S^T = K Q^T (keys x query rows), two independent accumulation chains
-      f32x16 sa = f32x16{}, sb = f32x16{};
-#pragma unroll
-      for (int s = 0; s < KSTEPS; s += 2) {
-        sa = mfma32(ka[s], qreg[s], sa);
-        sb = mfma32(ka[s + 1], qreg[s + 1], sb);
-      }
-      f32x16 sc = sa + sb;
-      const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
-      if (need_mask) {   // causal diagonal and sequence tail
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          const bool vis = key < T && (!a.causal || key <= qtok);
-          if (!vis) sc[i] = -INFINITY;
-        }
-      }
-      // ---- online softmax.  P = exp2(S*c - m) uses the current running maximum
-      // m as is; the half tile's row sums bound every P value (a lane's 16 values
-      // are non-negative), so if all sums stay <= 2^16 nothing overflows and m
-      // needs no update.  Otherwise (and on the first half tile, where m = -inf
-      // makes the sums infinite) a rare branch raises m to the true maximum,
-      // rescales O and l, and recomputes P.  Either way numerator and denominator
-      // share one reference, so the result is exact.
-      bf16x8 pp[2];
-      float lt;
-      exp_rows(sc, m, pp, lt);
-      if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT))) {
-        float mx = max16(sc);
-        mx = fmaxf(mx, partner32(mx, lo)) * c;
-        const float nm = fmaxf(m, mx);
-        const float alpha = (nm == -INFINITY) ? 1.f : fast_exp2(m - nm);
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
-        l *= alpha;
-        m = nm;
-        exp_rows(sc, nm == -INFINITY ? 0.f : nm, pp, lt);
-      }
-      l += lt;
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) o[db] = mfma32(va[ks][db], pp[ks], o[db]);
-    }
+    for (int s = 0; s < KSTEPS; ++s) ka[s] = *reinterpret_cast<const bf16x8*>(lds + kofs[s] + off);
   };
 
-  // ---- tile loop, unrolled by NBUF so each buffer index is a constant.  At
-  // tile t: request tile t+3 into the buffer of tile t-1 (every wave finished it
-  // before the barrier closing tile t-1), compute tile t, then publish tile t+1
-  // (the copies of tiles t+2 and t+3 may stay in flight).
+  // half tile h = 2t + KB, held in ring buffer BUF
+  auto half = [&](int t, auto kb_c, auto buf_c) {
+    constexpr int KB = decltype(kb_c)::value;
+    constexpr int BUF = decltype(buf_c)::value;
+    // LDS offset of the K half tile that follows this one
+    constexpr int KNEXT = KB == 0 ? BUF * TILE_BYTES + 32 * D * 2 : ((BUF + 1) % NBUF) * TILE_BYTES;
+    const int h = 2 * t + KB;
+    if (h > hl) return;
+    const int kbase_tok = 32 * h;
+
+    // ---- V^T operands of this half tile
+    bf16x8 va[2][DBLK];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const char* vp = lds + vofs[db] + BUF * TILE_BYTES + (KB * 32 + 16 * ks) * D * 2;
+        va[ks][db] = concat(lds_read_tr4(reinterpret_cast<const bf16*>(vp)),
+                            lds_read_tr4(reinterpret_cast<const bf16*>(vp + 8 * D * 2)));
+      }
+    // ---- S^T = K Q^T (keys x query rows)
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) sc = mfma32(ka[s], qreg[s], sc);
+    load_k(KNEXT);   // after the last half tile this reads unused (in-bounds) data
+    const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
+    if (need_mask) {   // causal diagonal and sequence tail
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const bool vis = key < T && (!a.causal || key <= qtok);
+        if (!vis) sc[i] = -INFINITY;
+      }
+    }
+    // ---- online softmax.  P = exp2(S*c - m) uses the current running maximum
+    // m as is; the half tile's row sums bound every P value (a lane's 16 values
+    // are non-negative), so if all sums stay <= 2^16 nothing overflows and m
+    // needs no update.  Otherwise (and on the first half tile, where m = -inf
+    // makes the sums infinite) a rare branch raises m to the true maximum,
+    // rescales O and l, and recomputes P.  Either way numerator and denominator
+    // share one reference, so the result is exact.
+    bf16x8 pp[2];
+    float lt;
+    exp_rows(sc, m, pp, lt);
+    if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT))) {
+      float mx = max16(sc);
+      mx = fmaxf(mx, partner32(mx, lo)) * c;
+      const float nm = fmaxf(m, mx);
+      const float alpha = (nm == -INFINITY) ? 1.f : fast_exp2(m - nm);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+      l *= alpha;
+      m = nm;
+      exp_rows(sc, nm == -INFINITY ? 0.f : nm, pp, lt);
+    }
+    l += lt;
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[db] = mfma32(va[ks][db], pp[ks], o[db]);
+  };
+
+  // ---- tile loop, unrolled by NBUF so each buffer index is a constant.  Tile t
+  // is read from the second half of tile t-1 (its first K half, read ahead) to
+  // its own second half.  The barrier between the two halves of tile t
+  // publishes tile t+1 (each wave waited for its own share of the copy) and
+  // proves that every wave finished tile t-1, whose buffer then receives tile
+  // t+3.
   dma_tile(0, 0);
   if (ntiles > 1) dma_tile(1, 1);
   if (ntiles > 2) dma_tile(2, 2);
   wait_vmcnt0_builtin();   // Q operands and the first tiles have landed
   __syncthreads();
+  load_k(0);
   auto tile = [&](int t, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    if (t + 3 < ntiles) dma_tile(t + 3, (BUF + 3) % NBUF);
-    if (active) compute_tile(t, bufc);
-    if (t + 3 < ntiles)
-      wait_vmcnt<4 * LOADS>();
-    else if (t + 2 < ntiles)
+    half(t, std::integral_constant<int, 0>{}, bufc);
+    if (t + 2 < ntiles)
       wait_vmcnt<2 * LOADS>();
     else
       wait_vmcnt<0>();
     __syncthreads();
+    if (t + 3 < ntiles) dma_tile(t + 3, (BUF + 3) % NBUF);
+    half(t, std::integral_constant<int, 1>{}, bufc);
   };
   for (int t = 0; t < ntiles; t += NBUF) {
     tile(t, std::integral_constant<int, 0>{});
