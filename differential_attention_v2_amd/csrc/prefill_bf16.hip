@@ -259,9 +259,13 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
                             lds_read_tr4(reinterpret_cast<const bf16*>(vp + 8 * D * 2)));
       }
     // ---- S^T = K Q^T (keys x query rows)
+    // raised issue priority while the S products issue: the other wave of the
+    // SIMD then tends to run its softmax meanwhile instead of interleaving MFMAs
     f32x16 sc = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) sc = mfma32(ka[s], qreg[s], sc);
+    __builtin_amdgcn_s_setprio(0);
     load_k(KNEXT);   // after the last half tile this reads unused (in-bounds) data
     const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
     if (need_mask) {   // causal diagonal and sequence tail
