@@ -22,6 +22,13 @@ pages on Differential Transformer V2; each function names its passage):
   "Differential Transformer V2 soll KI-Training stabiler machen", section
   "Gemeinsamer KV-Cache statt Spezialkernel"; lambda is a per-token, per-head
   sigmoid-bounded factor -- same article, "Weniger Ausreisser und Gradientenspitzen";
+* the causal sliding-window mask: key j visible to query i iff
+  max(0, i - window + 1) <= j <= i (window >= the sequence length restores the
+  full causal mask, window = 1 leaves each token only itself) -- attention-variants
+  lesson, "建立它 / 步骤2" (swa_mask); the same lesson's "用它" notes hybrids that
+  alternate DIFF attention with sliding-window layers, and serving engines are
+  integrating V2 (differential-attention lesson, "用它"), hence per-sequence cache
+  lengths in decode;
 * V1 reference mode: lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init and a
   per-head RMSNorm after the difference -- differential-attention lesson,
   "差异性概念" and "关键词" (lambda, per-head RMSNorm).
@@ -69,18 +76,22 @@ def _pair_heads(p: int, G: int) -> tuple[int, int, int]:
 
 
 def attention_weights(q_rows: np.ndarray, k: np.ndarray, row_pos: np.ndarray,
-                      causal: bool) -> np.ndarray:
+                      causal: bool, window: int = 0) -> np.ndarray:
     """Softmax(q k^T / sqrt(d)) for the given query rows of one head.
 
     q_rows [R, d] (fp64), k [N, d] (fp64), row_pos [R] = position of each query
     row in the key sequence.  Causal: key j visible iff j <= row_pos (the
-    attention-variants lesson's causal_mask).  Returns A [R, N].
+    attention-variants lesson's causal_mask); window > 0 (causal only) further
+    requires j >= row_pos - window + 1 (its swa_mask).  Returns A [R, N].
     """
     d = q_rows.shape[-1]
     s = (q_rows @ k.T) / math.sqrt(d)
+    j = np.arange(k.shape[0])[None, :]
     if causal:
-        j = np.arange(k.shape[0])[None, :]
         s = np.where(j <= row_pos[:, None], s, -np.inf)
+    if window > 0:
+        assert causal, "the sliding window is a causal mask"
+        s = np.where(j >= row_pos[:, None] - window + 1, s, -np.inf)
     return softmax_rows(s)
 
 
@@ -102,7 +113,8 @@ def v1_lambda(lq1, lk1, lq2, lk2, lambda_init: float = 0.8) -> np.ndarray:
 
 
 def diffattn_prefill(q, k, v, lam, causal: bool = True, v1_rmsnorm: bool = False,
-                     eps: float = DEFAULT_RMS_EPS, rows=None, row_block: int = 512) -> np.ndarray:
+                     eps: float = DEFAULT_RMS_EPS, rows=None, row_block: int = 512,
+                     window: int = 0) -> np.ndarray:
     """Differential attention over a whole sequence (prefill), fp64.
 
     q [B, T, Hq, d], k/v [B, T, Hkv, d], lam [B, T, P] (any real numbers, used as
@@ -132,20 +144,23 @@ def diffattn_prefill(q, k, v, lam, causal: bool = True, v1_rmsnorm: bool = False
             for r0 in range(0, rows.size, row_block):
                 rr = rows[r0:r0 + row_block]
                 n = int(rr.max()) + 1 if causal else T
-                a1 = attention_weights(q[b, rr, h1, :], kk[:n], rr, causal)
-                a2 = attention_weights(q[b, rr, h2, :], kk[:n], rr, causal)
+                a1 = attention_weights(q[b, rr, h1, :], kk[:n], rr, causal, window)
+                a2 = attention_weights(q[b, rr, h2, :], kk[:n], rr, causal, window)
                 x = a1 @ vv[:n] - lam[b, rr, p][:, None] * (a2 @ vv[:n])
                 out[b, r0:r0 + rr.size, p, :] = rmsnorm(x, eps) if v1_rmsnorm else x
     return out
 
 
 def diffattn_decode(q, k_cache, v_cache, lam, v1_rmsnorm: bool = False,
-                    eps: float = DEFAULT_RMS_EPS, batches=None, pairs=None) -> np.ndarray:
+                    eps: float = DEFAULT_RMS_EPS, batches=None, pairs=None,
+                    seq_lens=None, window: int = 0) -> np.ndarray:
     """Differential attention for one new query token per sequence over a KV cache.
 
-    q [B, Hq, d], k_cache/v_cache [B, L, Hkv, d], lam [B, P].  The query is the
-    token at position L-1 and every cache row is visible.  Same per-pair
-    arithmetic as ``diffattn_prefill``.  Returns out [len(batches), len(pairs), d].
+    q [B, Hq, d], k_cache/v_cache [B, L, Hkv, d], lam [B, P].  Sequence b holds
+    seq_lens[b] valid cache rows (all L if None); its query is the token at
+    position seq_lens[b]-1 and sees rows max(0, seq_lens[b] - window) ..
+    seq_lens[b]-1 (all of them if window = 0).  Same per-pair arithmetic as
+    ``diffattn_prefill``.  Returns out [len(batches), len(pairs), d].
     """
     q = np.asarray(q)
     B, Hq, d = q.shape
@@ -161,8 +176,10 @@ def diffattn_decode(q, k_cache, v_cache, lam, v1_rmsnorm: bool = False,
         for pi, p in enumerate(pairs):
             h1, h2, g = _pair_heads(int(p), G)
             if g not in kv_cache:
-                kv_cache = {g: (np.asarray(k_cache[b, :, g, :], dtype=np.float64),
-                                np.asarray(v_cache[b, :, g, :], dtype=np.float64))}
+                Lb = k_cache.shape[1] if seq_lens is None else int(seq_lens[b])
+                lo = max(0, Lb - window) if window > 0 else 0
+                kv_cache = {g: (np.asarray(k_cache[b, lo:Lb, g, :], dtype=np.float64),
+                                np.asarray(v_cache[b, lo:Lb, g, :], dtype=np.float64))}
             kk, vv = kv_cache[g]
             qq = np.asarray(q[b, [h1, h2], :], dtype=np.float64)
             a = attention_weights(qq, kk, np.array([kk.shape[0] - 1] * 2), causal=False)

@@ -305,3 +305,61 @@ def test_snr_gain_three_to_ten_fold():
         assert 2.9 <= min(g) and max(g) <= 10.6, (lam, g)
         assert abs(gains[lam] * (1 - lam) - 1) < 0.1
     assert gains[0.7] < gains[0.8] < gains[0.9]
+
+
+# --------------------------------------------------------------------------
+# sliding window and per-sequence cache lengths
+# --------------------------------------------------------------------------
+def _sdpa_mask(q, k, v, mask):
+    """torch fp64 SDPA of one head with an explicit boolean mask (True = visible)."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))[:, None]  # noqa: E731
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=torch.from_numpy(mask))
+    return o[:, 0].numpy()
+
+
+@pytest.mark.parametrize("window", [1, 5, 16, 40])
+def test_sliding_window_matches_masked_sdpa(window):
+    rng = np.random.default_rng(31 + window)
+    q, k, v, lam = _rand(rng, B=2, T=37, Hq=8, Hkv=2, d=16)
+    out = diffattn_prefill(q, k, v, lam, causal=True, window=window)
+    i = np.arange(37)[:, None]
+    j = np.arange(37)[None, :]
+    mask = (j <= i) & (j > i - window)          # the lesson's swa_mask, written as a predicate
+    G = 2
+    for p in range(4):
+        g = p // G
+        o1 = _sdpa_mask(q[:, :, 2 * p], k[:, :, g], v[:, :, g], mask)
+        o2 = _sdpa_mask(q[:, :, 2 * p + 1], k[:, :, g], v[:, :, g], mask)
+        np.testing.assert_allclose(out[:, :, p], o1 - lam[:, :, p][..., None] * o2, rtol=1e-12, atol=1e-12)
+
+
+def test_window_extremes():
+    rng = np.random.default_rng(41)
+    q, k, v, lam = _rand(rng, B=1, T=20, Hq=4, Hkv=1, d=8)
+    np.testing.assert_array_equal(diffattn_prefill(q, k, v, lam, window=20), diffattn_prefill(q, k, v, lam))
+    np.testing.assert_array_equal(diffattn_prefill(q, k, v, lam, window=1000), diffattn_prefill(q, k, v, lam))
+    # window 1: each token attends to itself only, so out = (1 - lambda) v_i
+    out = diffattn_prefill(q, k, v, lam, window=1)
+    np.testing.assert_allclose(out, (1.0 - lam)[..., None] * v[:, :, [0, 0]], rtol=1e-13, atol=1e-14)
+
+
+def test_decode_lengths_and_window_match_masked_sdpa():
+    rng = np.random.default_rng(43)
+    B, L, Hq, Hkv, d = 3, 50, 8, 2, 16
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, L, Hkv, d))
+    v = rng.standard_normal((B, L, Hkv, d))
+    lam = rng.uniform(0.2, 0.9, (B, Hq // 2))
+    lens = np.array([1, 17, 50])
+    for window in (0, 1, 8, 64):
+        out = diffattn_decode(q, k, v, lam, seq_lens=lens, window=window)
+        for b in range(B):
+            j = np.arange(L)
+            vis = (j < lens[b]) & ((j >= lens[b] - window) if window > 0 else True)
+            for p in range(Hq // 2):
+                g = p // 2
+                qq = q[b:b + 1, [2 * p, 2 * p + 1]].transpose(1, 0, 2)       # [2, 1, d]
+                kk = np.repeat(k[b:b + 1, :, g], 2, axis=0)
+                vv = np.repeat(v[b:b + 1, :, g], 2, axis=0)
+                o = _sdpa_mask(qq, kk, vv, vis[None, :])
+                np.testing.assert_allclose(out[b, p], o[0, 0] - lam[b, p] * o[1, 0], rtol=1e-12, atol=1e-12)
