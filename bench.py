@@ -89,8 +89,9 @@ def main() -> int:
                     help="untimed wall time of steps before the warmup steps (clock ramp-up); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one half of the step (for profiler runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
+                    help="time one part (for profiler runs); backward = training forward + backward only")
+    ap.add_argument("--no-backward", action="store_true", help="skip the training forward / backward timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (x5) to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -125,6 +126,7 @@ def main() -> int:
     wp, wd = W.CONFIGS[2], W.CONFIGS[4]
     do_p = args.only in (None, "prefill")
     do_d = args.only in (None, "decode")
+    do_b = args.only == "backward" or (args.only is None and not args.no_backward)
     if do_p:
         ip = W.make_prefill(wp)
         pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
@@ -170,6 +172,51 @@ def main() -> int:
     ms_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if do_p else None
     ms_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) if do_d else None
 
+    bwd = None
+    if do_b:
+        # training step of the attention core: training forward (out, o2, lse) and
+        # backward, timed after the main step, on the same c2 inputs
+        if not do_p:
+            ip = W.make_prefill(wp)
+            pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
+            plam = torch.from_numpy(ip["lam"]).to(dev)
+            del ip
+        bdout = dev_bf16(W.make_dout(wp))
+        tout, to2, tlse = bd.prefill_train(pq, pk, pv, plam)
+        bws = torch.empty(bd.diffattn_prefill_bwd_workspace_bytes(wp.B, wp.T, wp.Hq, wp.Hkv, wp.d),
+                          dtype=torch.uint8, device=dev)
+        grads = (torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv), torch.empty_like(plam))
+
+        def bstep(ev=None):
+            if ev: ev[0].record(stream)
+            bd.prefill_train(pq, pk, pv, plam)
+            if ev: ev[1].record(stream)
+            bd.prefill_backward(pq, pk, pv, plam, tout, to2, tlse, bdout, workspace=bws, grads=grads)
+            if ev: ev[2].record(stream)
+
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < min(args.settle_ms, 100.0):
+            for _ in range(5):
+                bstep()
+            torch.cuda.synchronize()
+        for _ in range(max(3, args.warmup // 5)):
+            bstep()
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            bstep(bev[i])
+        torch.cuda.synchronize()
+        ms_tf = float(np.mean([e[0].elapsed_time(e[1]) for e in bev]))
+        ms_bw = float(np.mean([e[1].elapsed_time(e[2]) for e in bev]))
+        bw_tf = wp.prefill_bwd_flops() / (ms_bw * 1e-3) / 1e12
+        bwd = {"value": bw_tf, "unit": "TFLOP/s", "frac": bw_tf / PEAK_BF16_TFLOPS, "ms_per_launch": ms_bw,
+               "algorithmic_flops_per_launch": wp.prefill_bwd_flops(),
+               "flop_count": "8*d per visible (query, key, head): dP, dV, dQ, dK products, no recompute",
+               "kernels": "bwd_pre + fill_zero + bwd_dkdv_kernel<128> + bwd_dq_kernel<128> + 2 x convert",
+               "train_forward_ms": ms_tf,
+               "train_forward_tflops": wp.prefill_flops() / (ms_tf * 1e-3) / 1e12,
+               "workload": f"{wp.name} causal bf16, dout ~ N(0,1)"}
+
     src_p = ["prefill_bf16.hip", "dev_common.h"]
     src_d = ["decode_bf16.hip", "dev_common.h"]
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -193,6 +240,10 @@ def main() -> int:
                                   "algorithmic_bytes_per_launch": wd.decode_kv_bytes()}
         if not do_p:
             res.update(value=gbs, unit="GB/s")
+    if bwd is not None:
+        res["backward"] = bwd
+        if not (do_p or do_d):
+            res.update(value=bwd["value"], unit="TFLOP/s")
     res["config"] = {"workload": (f"{wp.name}: B={wp.B} T={wp.T} Hq={wp.Hq} Hkv={wp.Hkv} d={wp.d} causal bf16"
                                   if do_p else None),
                      "decode_workload": wd.name if do_d else None,
@@ -201,7 +252,7 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "decode", "roofline_decode",
-             "cpu_baseline"]
+             "backward", "cpu_baseline"]
     print(json.dumps({k: res[k] for k in order if k in res}), flush=True)
     return 0
 

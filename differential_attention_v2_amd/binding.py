@@ -31,6 +31,10 @@ _SIGNATURES = {
                                       _c_int, _c_uint, _c_float, _vp]),
     "diffattn_decode_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, _c_uint, _c_float, _c_int, _vp, _c_size, _vp]),
+    "diffattn_prefill_fwd_window": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _c_int, _c_int, _c_uint, _c_float, _vp]),
+    "diffattn_decode_fwd_varlen": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_int, _c_uint, _c_float, _c_int, _vp, _c_size, _vp]),
     "diffattn_prefill_fwd_train": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                             _c_int, _c_int, _vp]),
     "diffattn_prefill_bwd": (_c_int, [_vp] * 12 + [_c_int] * 6 + [_vp, _c_size, _vp]),
@@ -77,6 +81,18 @@ def diffattn_decode_fwd(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, 
                         workspace, workspace_bytes, stream):
     return load_library().diffattn_decode_fwd(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, flags,
                                               rms_eps, num_splits, workspace, workspace_bytes, stream)
+
+
+def diffattn_prefill_fwd_window(q, k, v, lam, out, B, T, Hq, Hkv, d, window, dtype, flags, rms_eps, stream):
+    return load_library().diffattn_prefill_fwd_window(q, k, v, lam, out, B, T, Hq, Hkv, d, window, dtype, flags,
+                                                      rms_eps, stream)
+
+
+def diffattn_decode_fwd_varlen(q, k_cache, v_cache, lam, out, seq_lens, B, L, Hq, Hkv, d, window, dtype, flags,
+                               rms_eps, num_splits, workspace, workspace_bytes, stream):
+    return load_library().diffattn_decode_fwd_varlen(q, k_cache, v_cache, lam, out, seq_lens, B, L, Hq, Hkv, d,
+                                                     window, dtype, flags, rms_eps, num_splits, workspace,
+                                                     workspace_bytes, stream)
 
 
 def diffattn_prefill_fwd_train(q, k, v, lam, out, o2, lse, B, T, Hq, Hkv, d, causal, stream):
@@ -168,6 +184,54 @@ def prefill(q, k, v, lam, causal: bool = True, v1_rmsnorm: bool = False, eps: fl
                               DIFFATTN_FLAG_V1_RMSNORM if v1_rmsnorm else 0, float(eps), _stream(stream))
     if st != DIFFATTN_OK:
         raise DiffAttnError(st, "diffattn_prefill_fwd")
+    return out
+
+
+def prefill_window(q, k, v, lam, window: int, v1_rmsnorm: bool = False, eps: float = 1e-5, out=None,
+                   stream=None):
+    """out [B, T, P, d]: causal prefill where each query sees its last `window` keys (bf16)."""
+    torch = _torch()
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    _check(q, "q", (B, T, Hq, d), torch.bfloat16)
+    _check(k, "k", (B, T, Hkv, d), torch.bfloat16)
+    _check(v, "v", (B, T, Hkv, d), torch.bfloat16)
+    _check(lam, "lam", (B, T, Hq // 2), torch.float32)
+    if out is None:
+        out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device)
+    _check(out, "out", (B, T, Hq // 2, d), q.dtype)
+    st = diffattn_prefill_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(), out.data_ptr(), B, T,
+                                     Hq, Hkv, d, int(window), DIFFATTN_BF16,
+                                     DIFFATTN_FLAG_V1_RMSNORM if v1_rmsnorm else 0, float(eps), _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_prefill_fwd_window")
+    return out
+
+
+def decode_varlen(q, k_cache, v_cache, lam, seq_lens=None, window: int = 0, v1_rmsnorm: bool = False,
+                  eps: float = 1e-5, num_splits: int = 0, workspace=None, out=None, stream=None):
+    """out [B, P, d]: decode over caches with seq_lens[b] valid rows (int32 device tensor or None)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(q, "q", (B, Hq, d), torch.bfloat16)
+    _check(k_cache, "k_cache", (B, L, Hkv, d), torch.bfloat16)
+    _check(v_cache, "v_cache", (B, L, Hkv, d), torch.bfloat16)
+    _check(lam, "lam", (B, Hq // 2), torch.float32)
+    if seq_lens is not None:
+        _check(seq_lens, "seq_lens", (B,), torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq // 2, d), dtype=q.dtype, device=q.device)
+    _check(out, "out", (B, Hq // 2, d), q.dtype)
+    if workspace is None:
+        workspace = decode_workspace(B, L, Hq, Hkv, d, num_splits, q.device)
+    st = diffattn_decode_fwd_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lam.data_ptr(),
+                                    out.data_ptr(), None if seq_lens is None else seq_lens.data_ptr(), B, L, Hq,
+                                    Hkv, d, int(window), DIFFATTN_BF16, DIFFATTN_FLAG_V1_RMSNORM if v1_rmsnorm else 0,
+                                    float(eps), int(num_splits), workspace.data_ptr(), workspace.numel(),
+                                    _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_decode_fwd_varlen")
     return out
 
 

@@ -85,6 +85,23 @@ int diffattn_prefill_fwd(const void* q, const void* k, const void* v, const floa
   return hip_status(launch_prefill_bf16(p, s));
 }
 
+int diffattn_prefill_fwd_window(const void* q, const void* k, const void* v, const float* lambda, void* out,
+                                int B, int T, int Hq, int Hkv, int d, int window, int dtype, unsigned flags,
+                                float rms_eps, void* stream) {
+  if (B < 1 || T < 1 || window < 0) return DIFFATTN_ERR_INVALID_ARG;
+  int st = check_heads(Hq, Hkv, d);
+  if (st) return st;
+  st = check_mode(dtype, flags, rms_eps);
+  if (st) return st;
+  if (dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lambda, 4))
+    return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(B, T, Hq, d) || (long long)B * T * (Hq / 2) > kMaxGrid) return DIFFATTN_ERR_INVALID_ARG;
+  PrefillProblem p{q, k, v, lambda, out, B, T, Hq, Hkv, d, 1, (flags & DIFFATTN_FLAG_V1_RMSNORM) ? 1 : 0, rms_eps};
+  p.window = window >= T ? 0 : window;   // a window covering the sequence is plain causal
+  return hip_status(launch_prefill_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
 int diffattn_prefill_fwd_train(const void* q, const void* k, const void* v, const float* lambda, void* out,
                                void* o2, float* lse, int B, int T, int Hq, int Hkv, int d, int causal,
                                void* stream) {
@@ -165,6 +182,31 @@ int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
   DecodeProblem p{q, k_cache, v_cache, lambda, out, static_cast<float*>(workspace), B, L, Hq, Hkv, d, S, chunk,
                   v1, rms_eps};
   return hip_status(launch_decode_bf16(p, s));
+}
+
+int diffattn_decode_fwd_varlen(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
+                               void* out, const int* seq_lens, int B, int L, int Hq, int Hkv, int d, int window,
+                               int dtype, unsigned flags, float rms_eps, int num_splits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (B < 1 || L < 1 || num_splits < 0 || window < 0) return DIFFATTN_ERR_INVALID_ARG;
+  int st = check_heads(Hq, Hkv, d);
+  if (st) return st;
+  st = check_mode(dtype, flags, rms_eps);
+  if (st) return st;
+  if (dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(lambda, 4) || (seq_lens != nullptr && !aligned(seq_lens, 4)))
+    return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(B, L, Hkv, d) || !fits(B, Hq, d, 1)) return DIFFATTN_ERR_INVALID_ARG;
+  int S, chunk;
+  if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return DIFFATTN_ERR_INVALID_ARG;
+  const size_t need = (size_t)B * Hq * S * decode_record_floats(d) * sizeof(float);
+  if (!aligned(workspace, 16) || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+  DecodeProblem p{q, k_cache, v_cache, lambda, out, static_cast<float*>(workspace), B, L, Hq, Hkv, d, S, chunk,
+                  (flags & DIFFATTN_FLAG_V1_RMSNORM) ? 1 : 0, rms_eps};
+  p.seq_lens = seq_lens;
+  p.window = window;
+  return hip_status(launch_decode_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
 int diffattn_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2, float lambda_init,

@@ -40,6 +40,8 @@ struct Args {
   int S, chunk;
   int v1;
   float eps, scale_log2;
+  const int* seq_lens;   // valid rows per sequence, or null (all L)
+  int window;            // visible keys before and including the query, 0 = all
 };
 
 // V rows in LDS: row-major [key][d], 16-byte chunks XOR-permuted per row so the
@@ -69,8 +71,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
   const int g = blockIdx.x % a.Hkv;
   const int s = (blockIdx.x / a.Hkv) % a.S;
   const int b = blockIdx.x / (a.Hkv * a.S);
-  const int k0 = s * a.chunk;
-  const int k1 = min(a.L, k0 + a.chunk);
+  // keys this wave reads: its range of the cache, cut to the sequence's valid
+  // rows [lo, Lb) (lengths outside [1, L] are clamped, so every read stays in
+  // the cache); an empty range leaves m = -inf, l = 0, which the combine skips
+  const int Lb = a.seq_lens ? min(a.L, max(1, a.seq_lens[b])) : a.L;
+  const int lo = a.window > 0 ? max(0, Lb - a.window) : 0;
+  const int k0 = max(s * a.chunk, lo);
+  const int k1 = min(Lb, s * a.chunk + a.chunk);
 
   // Q^T operand: column n = head g*2G + n, d = 32*ks + 8*grp + 0..7
   bf16x8 qr[KS];
@@ -261,6 +268,8 @@ hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
   a.v1 = pr.v1_rmsnorm ? 1 : 0;
   a.eps = pr.eps;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  a.seq_lens = pr.seq_lens;
+  a.window = pr.window;
   const long long blocks = (long long)a.B * a.Hkv * a.S;
   hipLaunchKernelGGL(decode_split_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();

@@ -15,6 +15,7 @@ struct PrefillProblem {
   int causal;
   int v1_rmsnorm;
   float eps;
+  int window = 0;   // causal sliding window in keys, 0 = none (bf16 kernel)
   // training forward only (bf16, V2): the subtracted branch's output [B, T, P, d]
   // and the natural-log log-sum-exp of every row [B, T, Hq]; null otherwise
   void* o2 = nullptr;
@@ -33,6 +34,8 @@ struct DecodeProblem {
   int chunk;        // keys per range, a multiple of 32
   int v1_rmsnorm;
   float eps;
+  const int* seq_lens = nullptr;   // valid cache rows per sequence (device), or null = L
+  int window = 0;                  // keys before the query that stay visible, 0 = all
 };
 
 // Backward pass (bf16, V2).  The workspace holds, in order: per-pair row

@@ -54,6 +54,7 @@ struct Args {
   int B, T, Hq, Hkv, G, P;
   int causal, v1;
   float eps, scale_log2;
+  int window;  // causal sliding window in keys (0: none)
   int ppw;     // pairs per workgroup
   int nsub;    // 16-token sub-blocks per workgroup
   int chunks;  // workgroups needed to cover the G pairs of one KV head
@@ -140,8 +141,11 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   const int qtok = i0 + (l32 & 15);        // this lane's query token
   const int qhead = l32 >> 4;              // 0: positive branch, 1: subtracted branch
 
+  // key tiles [t_first, t_first + nt): with a sliding window the tiles that end
+  // before the window of the block's first token are never copied or read
   const int kv_end = a.causal ? min(T, tok0 + tokens_wg) : T;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  const int t_first = a.window > 0 ? max(0, tok0 - a.window + 1) / BN : 0;
+  const int nt = (kv_end + BN - 1) / BN - t_first;
   const bf16* kbase = a.k + ((size_t)b * T * a.Hkv + g) * D;
   const bf16* vbase = a.v + ((size_t)b * T * a.Hkv + g) * D;
 
@@ -232,6 +236,8 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   // Last 32-key half tile this wave reads; K operands are read one half tile
   // ahead into ka, right after the S products of the current one have issued.
   const int hl = active ? ((a.causal ? min(T, i0 + QT) : T) + 31) / 32 - 1 : -1;
+  // first half tile this wave reads (the window of its first token)
+  const int h_first = a.window > 0 ? max(0, i0 - a.window + 1) / 32 : 0;
   bf16x8 ka[KSTEPS];
   auto load_k = [&](int off) {
 #pragma unroll
@@ -245,7 +251,8 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
     // LDS offset of the K half tile that follows this one
     constexpr int KNEXT = KB == 0 ? BUF * TILE_BYTES + 32 * D * 2 : ((BUF + 1) % NBUF) * TILE_BYTES;
     const int h = 2 * t + KB;
-    if (h > hl) return;
+    if (h + 1 == h_first) load_k(KNEXT);   // the wave's first K operands
+    if (h < h_first || h > hl) return;
     const int kbase_tok = 32 * h;
 
     // ---- V^T operands of this half tile
@@ -267,12 +274,13 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
     for (int s = 0; s < KSTEPS; ++s) sc = mfma32(ka[s], qreg[s], sc);
     __builtin_amdgcn_s_setprio(0);
     load_k(KNEXT);   // after the last half tile this reads unused (in-bounds) data
-    const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
-    if (need_mask) {   // causal diagonal and sequence tail
+    const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T ||
+                           (a.window > 0 && kbase_tok + a.window <= i0 + QT - 1);
+    if (need_mask) {   // causal diagonal, sequence tail, window start
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const bool vis = key < T && (!a.causal || key <= qtok);
+        const bool vis = key < T && (!a.causal || key <= qtok) && (a.window == 0 || key > qtok - a.window);
         if (!vis) sc[i] = -INFINITY;
       }
     }
@@ -311,28 +319,30 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   // publishes tile t+1 (each wave waited for its own share of the copy) and
   // proves that every wave finished tile t-1, whose buffer then receives tile
   // t+3.
-  dma_tile(0, 0);
-  if (ntiles > 1) dma_tile(1, 1);
-  if (ntiles > 2) dma_tile(2, 2);
+  dma_tile(t_first, 0);
+  if (nt > 1) dma_tile(t_first + 1, 1);
+  if (nt > 2) dma_tile(t_first + 2, 2);
   wait_vmcnt0_builtin();   // Q operands and the first tiles have landed
   __syncthreads();
   load_k(0);
-  auto tile = [&](int t, auto bufc) {
+  // ring position r holds tile t_first + r in buffer r % NBUF
+  auto tile = [&](int r, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
+    const int t = t_first + r;
     half(t, std::integral_constant<int, 0>{}, bufc);
-    if (t + 2 < ntiles)
+    if (r + 2 < nt)
       wait_vmcnt<2 * LOADS>();
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (t + 3 < ntiles) dma_tile(t + 3, (BUF + 3) % NBUF);
+    if (r + 3 < nt) dma_tile(t + 3, (BUF + 3) % NBUF);
     half(t, std::integral_constant<int, 1>{}, bufc);
   };
-  for (int t = 0; t < ntiles; t += NBUF) {
-    tile(t, std::integral_constant<int, 0>{});
-    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
-    if (t + 2 < ntiles) tile(t + 2, std::integral_constant<int, 2>{});
-    if (t + 3 < ntiles) tile(t + 3, std::integral_constant<int, 3>{});
+  for (int r = 0; r < nt; r += NBUF) {
+    tile(r, std::integral_constant<int, 0>{});
+    if (r + 1 < nt) tile(r + 1, std::integral_constant<int, 1>{});
+    if (r + 2 < nt) tile(r + 2, std::integral_constant<int, 2>{});
+    if (r + 3 < nt) tile(r + 3, std::integral_constant<int, 3>{});
   }
 
   if (!active) return;
@@ -404,6 +414,7 @@ hipError_t launch(const PrefillProblem& pr, hipStream_t s) {
   a.causal = pr.causal ? 1 : 0;
   a.v1 = pr.v1_rmsnorm ? 1 : 0;
   a.eps = pr.eps;
+  a.window = pr.causal ? pr.window : 0;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   a.ppw = a.G < WAVES ? a.G : WAVES;
   a.nsub = WAVES / a.ppw;

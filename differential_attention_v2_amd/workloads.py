@@ -189,6 +189,11 @@ def make_decode(w: Workload) -> dict:
     return dict(q=q, k=k, v=v, lam=_sigmoid_f32(z))
 
 
+def ragged_lengths(B: int, L: int, seed: int = 4242) -> np.ndarray:
+    """Per-sequence cache lengths for ragged decode: uniform in [1, L], int32 [B]."""
+    return np.random.default_rng(seed).integers(1, L + 1, size=B, dtype=np.int32)
+
+
 def make_v1_lambda_vectors(P: int, d_lambda: int = 128, std: float = 0.1, seed: int = 2005) -> dict:
     """V1 reference-mode re-parameterisation vectors lq1, lk1, lq2, lk2 ~ N(0, std^2), fp32 [P, d_lambda]."""
     ss = np.random.SeedSequence(seed).spawn(4)

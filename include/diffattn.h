@@ -74,6 +74,19 @@ int diffattn_prefill_fwd(const void* q, const void* k, const void* v, const floa
                          int dtype, unsigned flags, float rms_eps, void* stream);
 
 /*
+ * Prefill with a causal sliding window (attention-variants lesson, "建立它 /
+ * 步骤2", swa_mask): key j is visible to query i iff max(0, i - window + 1) <= j
+ * <= i.  Key tiles wholly before a query block's window are neither copied nor
+ * read.  window = 0 or window >= T is the plain causal prefill.
+ *   q, k, v, lambda, out, flags, rms_eps   as diffattn_prefill_fwd; bf16 only
+ *   window  >= 0
+ * Returns a diffattn_status_t (fp32 -> DIFFATTN_ERR_UNSUPPORTED).
+ */
+int diffattn_prefill_fwd_window(const void* q, const void* k, const void* v, const float* lambda, void* out,
+                                int B, int T, int Hq, int Hkv, int d, int window, int dtype, unsigned flags,
+                                float rms_eps, void* stream);
+
+/*
  * Training forward (bf16, V2 map, no RMSNorm): the prefill above, plus what the
  * backward needs -- the subtracted branch's output and each row's log-sum-exp.
  *   q, k, v, lambda, out, causal   as diffattn_prefill_fwd (bf16 only)
@@ -134,6 +147,23 @@ int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
                         void* out, int B, int L, int Hq, int Hkv, int d,
                         int dtype, unsigned flags, float rms_eps, int num_splits,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode over ragged caches: sequence b holds seq_lens[b] valid rows of a cache
+ * allocated for L (its query is the token at row seq_lens[b]-1), and with
+ * window > 0 only its last `window` rows are visible.  Serving engines batch
+ * sequences of different lengths this way (the differential-attention lesson,
+ * "用它", notes V2 integration into serving engines).
+ *   seq_lens  device int32 [B], values in [1, L] (values outside are clamped),
+ *             or NULL: every sequence has L rows
+ *   window    >= 0, 0 = every valid row visible
+ *   other arguments as diffattn_decode_fwd (same workspace size); bf16 only
+ * Returns a diffattn_status_t (fp32 -> DIFFATTN_ERR_UNSUPPORTED).
+ */
+int diffattn_decode_fwd_varlen(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
+                               void* out, const int* seq_lens, int B, int L, int Hq, int Hkv, int d, int window,
+                               int dtype, unsigned flags, float rms_eps, int num_splits, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Split count the library picks for a decode problem (host only; no GPU call).
  * Returns 0 on invalid sizes. */
