@@ -89,9 +89,11 @@ def main() -> int:
                     help="untimed wall time of steps before the warmup steps (clock ramp-up); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
-                    help="time one part (for profiler runs); backward = training forward + backward only")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "serving"], default=None,
+                    help="time one part (for profiler runs); backward = training forward + backward, "
+                         "serving = windowed prefill + ragged decode")
     ap.add_argument("--no-backward", action="store_true", help="skip the training forward / backward timing")
+    ap.add_argument("--no-serving", action="store_true", help="skip the serving-variant timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (x5) to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -127,6 +129,7 @@ def main() -> int:
     do_p = args.only in (None, "prefill")
     do_d = args.only in (None, "decode")
     do_b = args.only == "backward" or (args.only is None and not args.no_backward)
+    do_s = args.only == "serving" or (args.only is None and not args.no_serving)
     if do_p:
         ip = W.make_prefill(wp)
         pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
@@ -213,9 +216,61 @@ def main() -> int:
                "algorithmic_flops_per_launch": wp.prefill_bwd_flops(),
                "flop_count": "8*d per visible (query, key, head): dP, dV, dQ, dK products, no recompute",
                "kernels": "bwd_pre + fill_zero + bwd_dkdv_kernel<128> + bwd_dq_kernel<128> + 2 x convert",
+               "traffic": _traffic("backward"),
                "train_forward_ms": ms_tf,
                "train_forward_tflops": wp.prefill_flops() / (ms_tf * 1e-3) / 1e12,
                "workload": f"{wp.name} causal bf16, dout ~ N(0,1)"}
+
+    serving = None
+    if do_s:
+        # serving variants on the same shapes: the c2 prefill with a 1024-key causal
+        # window, and the c4 decode over caches with lengths uniform in [1, 8192]
+        SWA = 1024
+        if not (do_p or do_b):
+            ip = W.make_prefill(wp)
+            pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
+            plam = torch.from_numpy(ip["lam"]).to(dev)
+            del ip
+        if not do_d:
+            idc = W.make_decode(wd)
+            dq, dk, dv = dev_bf16(idc["q"]), dev_bf16(idc["k"]), dev_bf16(idc["v"])
+            dlam = torch.from_numpy(idc["lam"]).to(dev)
+            dws = bd.decode_workspace(wd.B, wd.T, wd.Hq, wd.Hkv, wd.d, 0, dev)
+            del idc
+        sout = torch.empty((wp.B, wp.T, wp.P, wp.d), dtype=torch.bfloat16, device=dev)
+        lens_np = W.ragged_lengths(wd.B, wd.T)
+        lens = torch.from_numpy(lens_np).to(dev)
+        vout = torch.empty((wd.B, wd.P, wd.d), dtype=torch.bfloat16, device=dev)
+
+        def sstep(ev=None):
+            if ev: ev[0].record(stream)
+            bd.prefill_window(pq, pk, pv, plam, SWA, out=sout)
+            if ev: ev[1].record(stream)
+            bd.decode_varlen(dq, dk, dv, dlam, seq_lens=lens, workspace=dws, out=vout)
+            if ev: ev[2].record(stream)
+
+        for _ in range(max(3, args.warmup // 2)):
+            sstep()
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            sstep(sev[i])
+        torch.cuda.synchronize()
+        ms_sw = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
+        ms_vl = float(np.mean([e[1].elapsed_time(e[2]) for e in sev]))
+        vl_bytes = 2.0 * float(lens_np.sum()) * wd.Hkv * wd.d * 2
+        serving = {
+            "prefill_window": {"value": wp.prefill_flops(SWA) / (ms_sw * 1e-3) / 1e12, "unit": "TFLOP/s",
+                               "ms_per_launch": ms_sw, "window": SWA,
+                               "algorithmic_flops_per_launch": wp.prefill_flops(SWA),
+                               "frac": wp.prefill_flops(SWA) / (ms_sw * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                               "workload": f"{wp.name} causal, window {SWA}"},
+            "decode_varlen": {"value": vl_bytes / (ms_vl * 1e-3) / 1e9, "unit": "GB/s", "ms_per_launch": ms_vl,
+                              "traffic": _traffic("decode_varlen"),
+                              "algorithmic_bytes_per_launch": vl_bytes,
+                              "frac": vl_bytes / (ms_vl * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                              "workload": f"{wd.name} with lengths uniform in [1, {wd.T}] (mean "
+                                          f"{float(lens_np.mean()):.0f})"}}
 
     src_p = ["prefill_bf16.hip", "dev_common.h"]
     src_d = ["decode_bf16.hip", "dev_common.h"]
@@ -240,6 +295,8 @@ def main() -> int:
                                   "algorithmic_bytes_per_launch": wd.decode_kv_bytes()}
         if not do_p:
             res.update(value=gbs, unit="GB/s")
+    if serving is not None:
+        res["serving"] = serving
     if bwd is not None:
         res["backward"] = bwd
         if not (do_p or do_d):
@@ -252,7 +309,7 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "decode", "roofline_decode",
-             "backward", "cpu_baseline"]
+             "backward", "serving", "cpu_baseline"]
     print(json.dumps({k: res[k] for k in order if k in res}), flush=True)
     return 0
 

@@ -122,10 +122,14 @@ class Workload:
         return replace(self, **kw)
 
     # Algorithmic work, counted as the path defines it.
-    def prefill_flops(self) -> float:
-        """4*d flops per visible (query, key, head): QK^T and PV, 2*d each."""
+    def prefill_flops(self, window: int = 0) -> float:
+        """4*d flops per visible (query, key, head): QK^T and PV, 2*d each.  With a
+        causal sliding window, query i sees min(i + 1, window) keys."""
         T = self.T
-        pairs = T * (T + 1) / 2 if self.causal else T * T
+        if window > 0 and window < T:
+            pairs = window * (window + 1) / 2 + (T - window) * window
+        else:
+            pairs = T * (T + 1) / 2 if self.causal else T * T
         return 4.0 * self.d * self.Hq * self.B * pairs
 
     def prefill_bwd_flops(self) -> float:
