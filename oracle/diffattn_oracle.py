@@ -52,7 +52,7 @@ import numpy as np
 
 __all__ = [
     "softmax_rows", "attention_weights", "diffattn_prefill", "diffattn_decode",
-    "v1_lambda", "rmsnorm", "snr", "DEFAULT_RMS_EPS",
+    "v1_lambda", "rmsnorm", "snr", "DEFAULT_RMS_EPS", "standard_decode", "v1_layout_decode",
 ]
 
 DEFAULT_RMS_EPS = 1e-5
@@ -186,6 +186,61 @@ def diffattn_decode(q, k_cache, v_cache, lam, v1_rmsnorm: bool = False,
             o = a @ vv
             x = o[0] - float(lam[b, p]) * o[1]
             out[bi, pi] = rmsnorm(x[None], eps)[0] if v1_rmsnorm else x
+    return out
+
+
+def standard_decode(q, k_cache, v_cache, batches=None) -> np.ndarray:
+    """Baseline transformer decode: one softmax per query head, GQA.
+
+    q [B, H, d], k_cache/v_cache [B, L, Hkv, d]; head h reads KV head h // (H / Hkv);
+    out[b, h] = softmax(q k^T / sqrt(d)) v over all L rows (the standard attention
+    of the differential-attention lesson, "软max的噪音地板").  Returns [len(batches), H, d].
+    """
+    q = np.asarray(q)
+    B, H, d = q.shape
+    Hkv = k_cache.shape[2]
+    assert H % Hkv == 0
+    batches = np.arange(B) if batches is None else np.asarray(batches)
+    out = np.empty((batches.size, H, d))
+    for bi, b in enumerate(batches):
+        for g in range(Hkv):
+            kk = np.asarray(k_cache[b, :, g], np.float64)
+            vv = np.asarray(v_cache[b, :, g], np.float64)
+            hs = np.arange(g * (H // Hkv), (g + 1) * (H // Hkv))
+            a = attention_weights(np.asarray(q[b, hs], np.float64), kk, np.zeros(hs.size, np.int64), causal=False)
+            out[bi, hs] = a @ vv
+    return out
+
+
+def v1_layout_decode(q, k_cache, v_cache, lam, v1_rmsnorm: bool = True, eps: float = DEFAULT_RMS_EPS,
+                     batches=None) -> np.ndarray:
+    """DIFF V1 decode: each head's query and key are split into halves (Q1, Q2),
+    (K1, K2) of d/2 dims, A_r = softmax(Q_r K_r^T / sqrt(d/2)), out = (A1 - lam A2) V
+    with the head's full d-dim V, then the per-head RMSNorm -- differential-attention
+    lesson, "差异性概念" (split Q, K into two halves; the DiffAttn equation) and
+    "V1 vs V2" (V1 halves the per-branch head dim and applies per-head RMSNorm).
+    The scale uses the dot-product dimension d/2 (reading: the equation's d is the
+    dimension of the vectors in the dot product, as in the noise-floor formula).
+
+    q [B, H, d], k_cache/v_cache [B, L, Hkv, d], lam [B, H].  Returns [len(batches), H, d].
+    """
+    q = np.asarray(q)
+    B, H, d = q.shape
+    Hkv = k_cache.shape[2]
+    h2 = d // 2
+    batches = np.arange(B) if batches is None else np.asarray(batches)
+    out = np.empty((batches.size, H, d))
+    for bi, b in enumerate(batches):
+        for g in range(Hkv):
+            kk = np.asarray(k_cache[b, :, g], np.float64)
+            vv = np.asarray(v_cache[b, :, g], np.float64)
+            for h in range(g * (H // Hkv), (g + 1) * (H // Hkv)):
+                qh = np.asarray(q[b, h], np.float64)
+                z = np.zeros(1, np.int64)
+                a1 = attention_weights(qh[None, :h2], kk[:, :h2], z, causal=False)
+                a2 = attention_weights(qh[None, h2:], kk[:, h2:], z, causal=False)
+                x = (a1 - float(lam[b, h]) * a2) @ vv
+                out[bi, h] = (rmsnorm(x, eps) if v1_rmsnorm else x)[0]
     return out
 
 

@@ -363,3 +363,46 @@ def test_decode_lengths_and_window_match_masked_sdpa():
                 vv = np.repeat(v[b:b + 1, :, g], 2, axis=0)
                 o = _sdpa_mask(qq, kk, vv, vis[None, :])
                 np.testing.assert_allclose(out[b, p], o[0, 0] - lam[b, p] * o[1, 0], rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# decode layouts compared: standard transformer and DIFF V1
+# --------------------------------------------------------------------------
+from oracle import standard_decode, v1_layout_decode  # noqa: E402
+
+
+def test_standard_decode_matches_sdpa():
+    rng = np.random.default_rng(51)
+    B, L, H, Hkv, d = 2, 40, 8, 2, 16
+    q = rng.standard_normal((B, H, d))
+    k = rng.standard_normal((B, L, Hkv, d))
+    v = rng.standard_normal((B, L, Hkv, d))
+    out = standard_decode(q, k, v)
+    for h in range(H):
+        g = h // (H // Hkv)
+        ref = _sdpa(q[:, None, h], k[:, :, g], v[:, :, g], causal=False)[:, 0]
+        np.testing.assert_allclose(out[:, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_v1_layout_decode_pins():
+    rng = np.random.default_rng(52)
+    B, L, H, Hkv, d = 2, 30, 4, 2, 16
+    q = rng.standard_normal((B, H, d))
+    k = rng.standard_normal((B, L, Hkv, d))
+    v = rng.standard_normal((B, L, Hkv, d))
+    lam = rng.uniform(-0.3, 0.9, (B, H))
+    # lambda = 0, no norm: plain attention of the first halves (scale 1/sqrt(d/2)) over the full V
+    out0 = v1_layout_decode(q, k, v, np.zeros((B, H)), v1_rmsnorm=False)
+    for h in range(H):
+        g = h // 2
+        ref = _sdpa(q[:, None, h, :8], k[:, :, g, :8], v[:, :, g], causal=False)[:, 0]
+        np.testing.assert_allclose(out0[:, h], ref, rtol=1e-12, atol=1e-13)
+    # identical halves and lambda = 1 cancel exactly
+    qs = np.concatenate([q[..., :8], q[..., :8]], axis=-1)
+    ks = np.concatenate([k[..., :8], k[..., :8]], axis=-1)
+    assert np.max(np.abs(v1_layout_decode(qs, ks, v, np.ones((B, H)), v1_rmsnorm=False))) < 1e-13
+    # with the norm: rms of every head = sqrt(m / (m + eps)), direction of the raw difference kept
+    raw = v1_layout_decode(q, k, v, lam, v1_rmsnorm=False)
+    nrm = v1_layout_decode(q, k, v, lam, v1_rmsnorm=True, eps=1e-5)
+    m = np.mean(raw * raw, axis=-1, keepdims=True)
+    np.testing.assert_allclose(nrm, raw / np.sqrt(m + 1e-5), rtol=1e-12)
