@@ -89,11 +89,13 @@ def main() -> int:
                     help="untimed wall time of steps before the warmup steps (clock ramp-up); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "serving"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "serving", "layouts"], default=None,
                     help="time one part (for profiler runs); backward = training forward + backward, "
                          "serving = windowed prefill + ragged decode")
     ap.add_argument("--no-backward", action="store_true", help="skip the training forward / backward timing")
     ap.add_argument("--no-serving", action="store_true", help="skip the serving-variant timing")
+    ap.add_argument("--no-layouts", action="store_true",
+                    help="skip the decode layout comparison (standard transformer, DIFF V1, V2)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (x5) to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -130,6 +132,7 @@ def main() -> int:
     do_d = args.only in (None, "decode")
     do_b = args.only == "backward" or (args.only is None and not args.no_backward)
     do_s = args.only == "serving" or (args.only is None and not args.no_serving)
+    do_l = args.only == "layouts" or (args.only is None and not args.no_layouts)
     if do_p:
         ip = W.make_prefill(wp)
         pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
@@ -272,6 +275,51 @@ def main() -> int:
                               "workload": f"{wd.name} with lengths uniform in [1, {wd.T}] (mean "
                                           f"{float(lens_np.mean()):.0f})"}}
 
+    layouts = None
+    if do_l:
+        # decode-speed claim of the pages: on the c4 cache geometry (B=64, L=8192,
+        # Hkv=8, d=128) time a standard transformer with H=32 heads, DIFF V1 with
+        # the same 32 heads (q, k halves per branch, V read once per branch) and V2
+        # (64 query heads = 32 pairs, the bench's decode)
+        H = wd.P
+        ic = W.make_compare_decode(wd.B, wd.T, H, wd.Hkv, wd.d, seed=9300)
+        cq, ck, cv = dev_bf16(ic["q"]), dev_bf16(ic["k"]), dev_bf16(ic["v"])
+        clam = torch.from_numpy(ic["lam"]).to(dev)
+        del ic
+        if not do_d:
+            idc = W.make_decode(wd)
+            dq, dk, dv = dev_bf16(idc["q"]), dev_bf16(idc["k"]), dev_bf16(idc["v"])
+            dlam = torch.from_numpy(idc["lam"]).to(dev)
+            dws = bd.decode_workspace(wd.B, wd.T, wd.Hq, wd.Hkv, wd.d, 0, dev)
+            del idc
+        cws = torch.empty(bd.diffattn_decode_compare_workspace_bytes(wd.B, wd.T, H, wd.Hkv, wd.d, 0),
+                          dtype=torch.uint8, device=dev)
+        cout = torch.empty((wd.B, H, wd.d), dtype=torch.bfloat16, device=dev)
+        v2out = torch.empty((wd.B, wd.P, wd.d), dtype=torch.bfloat16, device=dev)
+        runs = {"standard": lambda: bd.decode_standard(cq, ck, cv, workspace=cws, out=cout),
+                "v1_layout": lambda: bd.decode_v1_layout(cq, ck, cv, clam, workspace=cws, out=cout),
+                "v2": lambda: bd.decode(dq, dk, dv, dlam, workspace=dws, out=v2out)}
+        cache = wd.B * wd.T * wd.Hkv * wd.d * 2
+        bytes_read = {"standard": 2.0 * cache, "v1_layout": 3.0 * cache, "v2": 2.0 * cache}
+        layouts = {}
+        for name, fn in runs.items():
+            for _ in range(max(3, args.warmup // 2)):
+                fn()
+            lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                lev[i][0].record(stream)
+                fn()
+                lev[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([e[0].elapsed_time(e[1]) for e in lev]))
+            layouts[name] = {"ms_per_launch": ms, "cache_bytes_read": bytes_read[name],
+                             "GB_per_s": bytes_read[name] / (ms * 1e-3) / 1e9}
+        for name in ("v1_layout", "v2"):
+            layouts[name]["time_vs_standard"] = layouts[name]["ms_per_launch"] / layouts["standard"]["ms_per_launch"]
+        layouts["workload"] = (f"B={wd.B} L={wd.T} Hkv={wd.Hkv} d={wd.d} bf16 cache; standard and V1: {H} heads; "
+                               f"V2: {wd.Hq} query heads ({wd.P} pairs)")
+
     src_p = ["prefill_bf16.hip", "dev_common.h"]
     src_d = ["decode_bf16.hip", "dev_common.h"]
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -297,6 +345,8 @@ def main() -> int:
             res.update(value=gbs, unit="GB/s")
     if serving is not None:
         res["serving"] = serving
+    if layouts is not None:
+        res["decode_layouts"] = layouts
     if bwd is not None:
         res["backward"] = bwd
         if not (do_p or do_d):
@@ -309,7 +359,7 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "decode", "roofline_decode",
-             "backward", "serving", "cpu_baseline"]
+             "backward", "serving", "decode_layouts", "cpu_baseline"]
     print(json.dumps({k: res[k] for k in order if k in res}), flush=True)
     return 0
 

@@ -39,6 +39,9 @@ _SIGNATURES = {
                                             _c_int, _c_int, _vp]),
     "diffattn_prefill_bwd": (_c_int, [_vp] * 12 + [_c_int] * 6 + [_vp, _c_size, _vp]),
     "diffattn_prefill_bwd_workspace_bytes": (_c_size, [_c_int] * 5),
+    "diffattn_decode_standard": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 6 + [_vp, _c_size, _vp]),
+    "diffattn_decode_v1_layout": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_c_uint, _c_float, _c_int, _vp, _c_size, _vp]),
+    "diffattn_decode_compare_workspace_bytes": (_c_size, [_c_int] * 6),
     "diffattn_decode_num_splits": (_c_int, [_c_int] * 5),
     "diffattn_decode_workspace_bytes": (_c_size, [_c_int] * 6),
     "diffattn_v1_lambda": (_c_int, [_vp, _vp, _vp, _vp, _c_float, _vp, _c_int, _c_int, _c_int, _vp]),
@@ -107,6 +110,22 @@ def diffattn_prefill_bwd(q, k, v, lam, out, o2, lse, dout, dq, dk, dv, dlam, B, 
 
 def diffattn_prefill_bwd_workspace_bytes(B, T, Hq, Hkv, d):
     return load_library().diffattn_prefill_bwd_workspace_bytes(B, T, Hq, Hkv, d)
+
+
+def diffattn_decode_standard(q, k_cache, v_cache, out, B, L, H, Hkv, d, num_splits, workspace, workspace_bytes,
+                             stream):
+    return load_library().diffattn_decode_standard(q, k_cache, v_cache, out, B, L, H, Hkv, d, num_splits, workspace,
+                                                   workspace_bytes, stream)
+
+
+def diffattn_decode_v1_layout(q, k_cache, v_cache, lam, out, B, L, H, Hkv, d, flags, rms_eps, num_splits, workspace,
+                              workspace_bytes, stream):
+    return load_library().diffattn_decode_v1_layout(q, k_cache, v_cache, lam, out, B, L, H, Hkv, d, flags, rms_eps,
+                                                    num_splits, workspace, workspace_bytes, stream)
+
+
+def diffattn_decode_compare_workspace_bytes(B, L, H, Hkv, d, num_splits=0):
+    return load_library().diffattn_decode_compare_workspace_bytes(B, L, H, Hkv, d, num_splits)
 
 
 def diffattn_decode_num_splits(B, L, Hq, Hkv, d):
@@ -232,6 +251,50 @@ def decode_varlen(q, k_cache, v_cache, lam, seq_lens=None, window: int = 0, v1_r
                                     _stream(stream))
     if st != DIFFATTN_OK:
         raise DiffAttnError(st, "diffattn_decode_fwd_varlen")
+    return out
+
+
+def decode_standard(q, k_cache, v_cache, num_splits: int = 0, workspace=None, out=None, stream=None):
+    """out [B, H, d]: standard-transformer decode (one softmax per head) over bf16 caches."""
+    torch = _torch()
+    B, H, d = q.shape
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(q, "q", (B, H, d), torch.bfloat16)
+    _check(k_cache, "k_cache", (B, L, Hkv, d), torch.bfloat16)
+    _check(v_cache, "v_cache", (B, L, Hkv, d), torch.bfloat16)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(diffattn_decode_compare_workspace_bytes(B, L, H, Hkv, d, num_splits),
+                                dtype=torch.uint8, device=q.device)
+    st = diffattn_decode_standard(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), B, L, H, Hkv,
+                                  d, int(num_splits), workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_decode_standard")
+    return out
+
+
+def decode_v1_layout(q, k_cache, v_cache, lam, v1_rmsnorm: bool = True, eps: float = 1e-5, num_splits: int = 0,
+                     workspace=None, out=None, stream=None):
+    """out [B, H, d]: DIFF V1 decode (q, k split into halves per branch, V read once per branch)."""
+    torch = _torch()
+    B, H, d = q.shape
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(q, "q", (B, H, d), torch.bfloat16)
+    _check(k_cache, "k_cache", (B, L, Hkv, d), torch.bfloat16)
+    _check(v_cache, "v_cache", (B, L, Hkv, d), torch.bfloat16)
+    _check(lam, "lam", (B, H), torch.float32)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(diffattn_decode_compare_workspace_bytes(B, L, H, Hkv, d, num_splits),
+                                dtype=torch.uint8, device=q.device)
+    st = diffattn_decode_v1_layout(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lam.data_ptr(),
+                                   out.data_ptr(), B, L, H, Hkv, d, DIFFATTN_FLAG_V1_RMSNORM if v1_rmsnorm else 0,
+                                   float(eps), int(num_splits), workspace.data_ptr(), workspace.numel(),
+                                   _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_decode_v1_layout")
     return out
 
 

@@ -209,6 +209,49 @@ int diffattn_decode_fwd_varlen(const void* q, const void* k_cache, const void* v
   return hip_status(launch_decode_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t diffattn_decode_compare_workspace_bytes(int B, int L, int H, int Hkv, int d, int num_splits) {
+  if (B < 1 || L < 1 || Hkv < 1 || H < 1 || H % Hkv != 0 || H / Hkv > 16 || (d != 64 && d != 128)) return 0;
+  int S, chunk;
+  if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return 0;
+  return 2 * (size_t)B * H * S * decode_record_floats(d) * sizeof(float);
+}
+
+namespace {
+int decode_compare(const void* q, const void* k_cache, const void* v_cache, const float* lambda, void* out, int B,
+                   int L, int H, int Hkv, int d, int v1_layout, unsigned flags, float rms_eps, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || L < 1 || num_splits < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return DIFFATTN_ERR_INVALID_ARG;
+  if (d <= 0) return DIFFATTN_ERR_INVALID_ARG;
+  if ((d != 64 && d != 128) || H / Hkv > 16) return DIFFATTN_ERR_UNSUPPORTED;
+  int st = check_mode(DIFFATTN_BF16, flags, rms_eps);
+  if (st) return st;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      (v1_layout && !aligned(lambda, 4)))
+    return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(B, L, Hkv, d) || !fits(B, H, d, 1)) return DIFFATTN_ERR_INVALID_ARG;
+  int S, chunk;
+  if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return DIFFATTN_ERR_INVALID_ARG;
+  const size_t need = (v1_layout ? 2 : 1) * (size_t)B * H * S * decode_record_floats(d) * sizeof(float);
+  if (!aligned(workspace, 16) || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+  CompareProblem p{q, k_cache, v_cache, lambda, out, static_cast<float*>(workspace), B, L, H, Hkv, d, S, chunk,
+                   v1_layout, (flags & DIFFATTN_FLAG_V1_RMSNORM) ? 1 : 0, rms_eps};
+  return hip_status(launch_decode_compare_bf16(p, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int diffattn_decode_standard(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int L, int H,
+                             int Hkv, int d, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_compare(q, k_cache, v_cache, nullptr, out, B, L, H, Hkv, d, 0, 0u, 1e-5f, num_splits, workspace,
+                        workspace_bytes, stream);
+}
+
+int diffattn_decode_v1_layout(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
+                              void* out, int B, int L, int H, int Hkv, int d, unsigned flags, float rms_eps,
+                              int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_compare(q, k_cache, v_cache, lambda, out, B, L, H, Hkv, d, 1, flags, rms_eps, num_splits, workspace,
+                        workspace_bytes, stream);
+}
+
 int diffattn_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2, float lambda_init,
                        float* lambda_out, int P, int d_lambda, int rows, void* stream) {
   if (P < 1 || d_lambda < 1 || rows < 1 || !std::isfinite(lambda_init)) return DIFFATTN_ERR_INVALID_ARG;

@@ -21,6 +21,13 @@
 // Combine kernel: one wave per (b, pair).  For both heads of the pair it
 // merges the partial states (M = max_s m_s, weights 2^(m_s - M)), normalises,
 // forms o_1 - lambda * o_2 (optional V1 RMSNorm) and writes bf16.
+//
+// The split kernel is written for any number nq <= 16 of query heads per KV head
+// and any dot-product slice [off, off + DK) of the q and k rows, so the same code
+// also runs the two layouts V2 is compared against (differential-attention
+// lesson, section "V1 vs V2"): a standard transformer (one softmax per head, H
+// heads) and DIFF V1 (each head's q and k split into halves of d/2, one pass per
+// branch, each pass reading the full V rows -- V is read twice per step).
 #include "dev_common.h"
 #include "internal.h"
 
@@ -42,6 +49,8 @@ struct Args {
   float eps, scale_log2;
   const int* seq_lens;   // valid rows per sequence, or null (all L)
   int window;            // visible keys before and including the query, 0 = all
+  int nq;                // query heads per KV head served by one wave (<= 16)
+  int qoff, koff;        // start of the dot-product slice within q and k rows
 };
 
 // V rows in LDS: row-major [key][d], 16-byte chunks XOR-permuted per row so the
@@ -53,9 +62,9 @@ __device__ __forceinline__ int v_phys(int row, int col) {
   return row * D + ((((col >> 3) ^ sw)) << 3) + (col & 7);
 }
 
-template <int D>
+template <int D, int DK>
 __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
-  constexpr int KS = D / 32;                 // QK^T k-steps (k = 32 per MFMA)
+  constexpr int KS = DK / 32;                // QK^T k-steps (k = 32 per MFMA)
   constexpr int DB = D / 16;                 // PV d-blocks (16 rows per MFMA)
   constexpr int NCH = D / 8;                 // 16-byte chunks per cache row
   constexpr int VLOADS = KSTEP * NCH / 64;   // V chunks per lane per step
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
   const int lane = threadIdx.x;
   const int n = lane & 15;     // query column = head within the group
   const int grp = lane >> 4;   // 16-lane group
-  const int nq = 2 * a.G;
+  const int nq = a.nq;
 
   // KV head fastest: the Hkv waves of one (b, key range) are dispatched together
   // and stream neighbouring 256-byte pieces of the same cache rows.
@@ -83,7 +92,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
   bf16x8 qr[KS];
   {
     const bool ok = n < nq;
-    const bf16* src = a.q + ((size_t)b * a.Hq + g * nq + (ok ? n : 0)) * D + 8 * grp;
+    const bf16* src = a.q + ((size_t)b * a.Hq + g * nq + (ok ? n : 0)) * D + a.qoff + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 x = ok ? ldg16(src + 32 * ks) : u32x4{0, 0, 0, 0};
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
     for (int h = 0; h < 2; ++h) {
       const int key = kk + 16 * h + n;
       const bool ok = key < k1;
-      const bf16* src = kb0 + (size_t)(ok ? key : k0) * row + 8 * grp;
+      const bf16* src = kb0 + (size_t)(ok ? key : k0) * row + a.koff + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ka[h][ks] = ok ? ldg16_stream(src + 32 * ks) : u32x4{0, 0, 0, 0};
     }
@@ -189,47 +198,52 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
   }
 }
 
-// One wave per (b, pair); lane owns D/64 consecutive output columns.  All
-// partial states of both heads are requested before any is used, so the kernel
-// costs about one memory round trip.
+// Merge the S partial states of one query head (records at base): lane owns
+// D/64 consecutive columns of the normalised output.  All records are requested
+// before any is used, so a merge costs about one memory round trip.
+template <int D>
+__device__ __forceinline__ void merge_head(const float* base, int S, int lane, float (&o)[D / 64]) {
+  constexpr int E = D / 64;
+  constexpr int UNR = 8;               // key ranges in flight per batch of loads
+  const int rec = D + 4;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, base[s * rec + D]);
+  float acc[E], den = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += UNR) {
+    float ms[UNR], ls[UNR], av[UNR][E];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int s = min(s0 + u, S - 1);
+      ms[u] = base[s * rec + D];
+      ls[u] = base[s * rec + D + 1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) av[u][e] = base[s * rec + E * lane + e];
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const float wgt = (s0 + u >= S || ms[u] == -INFINITY) ? 0.f : fast_exp2(ms[u] - M);
+      den += wgt * ls[u];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += wgt * av[u][e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = acc[e] / den;
+}
+
+// One wave per (b, pair): o_1 - lambda o_2 (optional V1 RMSNorm), bf16 out.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(Args a) {
   constexpr int E = D / 64;            // columns per lane
-  constexpr int UNR = 8;               // key ranges in flight per batch of loads
   const int bp = blockIdx.x;
   const int b = bp / a.P, p = bp % a.P;
   const int lane = threadIdx.x;
   const int rec = D + 4;
   float o[2][E];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float* base = a.ws + ((size_t)b * a.Hq + 2 * p + h) * a.S * rec;
-    float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s) M = fmaxf(M, base[s * rec + D]);
-    float acc[E], den = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int s0 = 0; s0 < a.S; s0 += UNR) {
-      float ms[UNR], ls[UNR], av[UNR][E];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int s = min(s0 + u, a.S - 1);
-        ms[u] = base[s * rec + D];
-        ls[u] = base[s * rec + D + 1];
-#pragma unroll
-        for (int e = 0; e < E; ++e) av[u][e] = base[s * rec + E * lane + e];
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const float wgt = (s0 + u >= a.S || ms[u] == -INFINITY) ? 0.f : fast_exp2(ms[u] - M);
-        den += wgt * ls[u];
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += wgt * av[u][e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[h][e] = acc[e] / den;
-  }
+  for (int h = 0; h < 2; ++h) merge_head<D>(a.ws + ((size_t)b * a.Hq + 2 * p + h) * a.S * rec, a.S, lane, o[h]);
   const float lamv = a.lam[(size_t)b * a.P + p];
   float x[E], ss = 0.f;
 #pragma unroll
@@ -244,6 +258,40 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(Args a) {
     for (int e = 0; e < E; ++e) x[e] *= r;
   }
   bf16* dst = a.out + ((size_t)b * a.P + p) * D + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[e] = (bf16)x[e];
+}
+
+// Comparison layouts: one wave per (b, head).  Standard transformer: the head's
+// merged output.  DIFF V1: (branch-1 output) - lambda[b, h] (branch-2 output),
+// optional per-head RMSNorm; ws2 holds the second branch's records.
+template <int D>
+__global__ __launch_bounds__(64) void compare_combine_kernel(Args a, const float* ws2) {
+  constexpr int E = D / 64;
+  const int bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int rec = D + 4;
+  float o1[E], o2[E];
+  merge_head<D>(a.ws + (size_t)bh * a.S * rec, a.S, lane, o1);
+  float x[E], ss = 0.f;
+  if (ws2 != nullptr) {
+    merge_head<D>(ws2 + (size_t)bh * a.S * rec, a.S, lane, o2);
+    const float lamv = a.lam[bh];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = o1[e] - lamv * o2[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = o1[e];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) ss += x[e] * x[e];
+  if (a.v1) {
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] *= r;
+  }
+  bf16* dst = a.out + (size_t)bh * D + E * lane;
 #pragma unroll
   for (int e = 0; e < E; ++e) dst[e] = (bf16)x[e];
 }
@@ -270,11 +318,59 @@ hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   a.seq_lens = pr.seq_lens;
   a.window = pr.window;
+  a.nq = 2 * a.G;
+  a.qoff = a.koff = 0;
   const long long blocks = (long long)a.B * a.Hkv * a.S;
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3((unsigned)blocks), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, D>), dim3((unsigned)blocks), dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.B * a.P)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_compare(const CompareProblem& pr, hipStream_t st) {
+  Args a{};
+  a.q = static_cast<const bf16*>(pr.q);
+  a.k = static_cast<const bf16*>(pr.k);
+  a.v = static_cast<const bf16*>(pr.v);
+  a.lam = pr.lam;
+  a.out = static_cast<bf16*>(pr.out);
+  a.ws = pr.ws;
+  a.B = pr.B;
+  a.L = pr.L;
+  a.Hq = pr.H;
+  a.Hkv = pr.Hkv;
+  a.S = pr.splits;
+  a.chunk = pr.chunk;
+  a.v1 = pr.v1_rmsnorm ? 1 : 0;
+  a.eps = pr.eps;
+  a.seq_lens = nullptr;
+  a.window = 0;
+  a.nq = pr.H / pr.Hkv;
+  const long long blocks = (long long)a.B * a.Hkv * a.S;
+  float* ws2 = nullptr;
+  if (!pr.v1_layout) {   // standard transformer: one pass, dot products over all D dims
+    a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+    a.qoff = a.koff = 0;
+    hipLaunchKernelGGL((decode_split_kernel<D, D>), dim3((unsigned)blocks), dim3(64), 0, st, a);
+  } else {               // DIFF V1: one pass per branch over its half of q and k, V in full each time
+    constexpr int DH = D / 2;
+    a.scale_log2 = 1.4426950408889634f / sqrtf((float)DH);
+    a.qoff = a.koff = 0;
+    hipLaunchKernelGGL((decode_split_kernel<D, DH>), dim3((unsigned)blocks), dim3(64), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    Args a2 = a;
+    ws2 = pr.ws + (size_t)pr.B * pr.H * pr.splits * (D + 4);
+    a2.ws = ws2;
+    a2.qoff = a2.koff = DH;
+    hipLaunchKernelGGL((decode_split_kernel<D, DH>), dim3((unsigned)blocks), dim3(64), 0, st, a2);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compare_combine_kernel<D>, dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, st, a,
+                     static_cast<const float*>(ws2));
   return hipGetLastError();
 }
 
@@ -282,6 +378,10 @@ hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
 
 hipError_t launch_decode_bf16(const DecodeProblem& p, hipStream_t s) {
   return p.d == 128 ? launch<128>(p, s) : launch<64>(p, s);
+}
+
+hipError_t launch_decode_compare_bf16(const CompareProblem& p, hipStream_t s) {
+  return p.d == 128 ? launch_compare<128>(p, s) : launch_compare<64>(p, s);
 }
 
 }  // namespace diffattn

@@ -38,6 +38,24 @@ struct DecodeProblem {
   int window = 0;                  // keys before the query that stay visible, 0 = all
 };
 
+// Decode in the layouts V2 is compared against: a standard transformer (H heads,
+// one softmax each) or DIFF V1 (each head's q and k split into halves, one pass
+// per branch over the full V).  q [B, H, d], caches [B, L, Hkv, d], lam [B, H]
+// (V1), out [B, H, d]; ws holds one [B, H, splits, d+4] record array per pass.
+struct CompareProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* lam;
+  void* out;
+  float* ws;
+  int B, L, H, Hkv, d;
+  int splits, chunk;
+  int v1_layout;
+  int v1_rmsnorm;
+  float eps;
+};
+
 // Backward pass (bf16, V2).  The workspace holds, in order: per-pair row
 // statistics [B][P][5][Tpad] fp32 (log2-domain LSE of both heads, D_1, D_2,
 // lambda; Tpad = T rounded up to 32), then fp32 dK and dV accumulators
@@ -75,6 +93,7 @@ inline int decode_record_floats(int d) { return d + 4; }
 hipError_t launch_prefill_bf16(const PrefillProblem& p, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeProblem& p, hipStream_t s);
 hipError_t launch_backward_bf16(const BackwardProblem& p, hipStream_t s);
+hipError_t launch_decode_compare_bf16(const CompareProblem& p, hipStream_t s);
 // fp32 path: rows of queries [B, Tq] over Tk keys; causal limit j <= i + (Tk - Tq).
 hipError_t launch_rows_f32(const PrefillProblem& p, int Tq, int Tk, hipStream_t s);
 hipError_t launch_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,

@@ -193,6 +193,18 @@ def make_decode(w: Workload) -> dict:
     return dict(q=q, k=k, v=v, lam=_sigmoid_f32(z))
 
 
+def make_compare_decode(B: int, L: int, H: int, Hkv: int, d: int, seed: int) -> dict:
+    """Inputs for the decode layout comparison: q [B, H, d], caches [B, L, Hkv, d]
+    (bf16 bits, N(0, 1)) and a per-head lambda [B, H] uniform in [-0.3, 0.9]
+    (V1's lambda may be negative)."""
+    s = _streams(seed)
+    q = _normal(s[_S_Q], B * H * d, 1.0, "bf16").reshape(B, H, d)
+    k = _normal(s[_S_K], B * L * Hkv * d, 1.0, "bf16").reshape(B, L, Hkv, d)
+    v = _normal(s[_S_V], B * L * Hkv * d, 1.0, "bf16").reshape(B, L, Hkv, d)
+    lam = np.random.default_rng(s[_S_LAM]).uniform(-0.3, 0.9, (B, H)).astype(np.float32)
+    return dict(q=q, k=k, v=v, lam=lam)
+
+
 def ragged_lengths(B: int, L: int, seed: int = 4242) -> np.ndarray:
     """Per-sequence cache lengths for ragged decode: uniform in [1, L], int32 [B]."""
     return np.random.default_rng(seed).integers(1, L + 1, size=B, dtype=np.int32)

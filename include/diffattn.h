@@ -165,6 +165,34 @@ int diffattn_decode_fwd_varlen(const void* q, const void* k_cache, const void* v
                                int dtype, unsigned flags, float rms_eps, int num_splits, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Decode in the layouts V2 is measured against (differential-attention lesson,
+ * section "V1 vs V2": V1 halves the per-branch head dim and must load the value
+ * cache twice per decode step, once per softmax branch, so it decodes slower
+ * than a standard transformer; V2 loads the KV cache once and matches it).
+ * Both use the same cache geometry as diffattn_decode_fwd and its split plan.
+ *
+ * diffattn_decode_standard: standard transformer decode, H query heads over Hkv
+ * KV heads (GQA), out[b,h] = softmax(q_h k^T / sqrt(d)) v.
+ *   q device [B, H, d] bf16, caches [B, L, Hkv, d] bf16, out [B, H, d] bf16
+ * diffattn_decode_v1_layout: DIFF V1 decode; head h's q and k rows split into
+ * halves (q1 | q2), (k1 | k2) of d/2, A_r = softmax(q_r k_r^T / sqrt(d/2)),
+ * out = (A_1 - lambda[b,h] A_2) v with the full d-dim v, then the per-head
+ * RMSNorm when flags has DIFFATTN_FLAG_V1_RMSNORM.  Runs one pass per branch,
+ * each reading its half of K and all of V.
+ *   lambda device [B, H] fp32
+ * Constraints: H % Hkv == 0, H / Hkv <= 16, d in {64, 128}; bf16 only.
+ * workspace >= diffattn_decode_compare_workspace_bytes(...) bytes, 16-byte aligned.
+ * Return a diffattn_status_t.
+ */
+int diffattn_decode_standard(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int L, int H,
+                             int Hkv, int d, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+int diffattn_decode_v1_layout(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
+                              void* out, int B, int L, int H, int Hkv, int d, unsigned flags, float rms_eps,
+                              int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes for either comparison decode (host only; 0 on invalid sizes). */
+size_t diffattn_decode_compare_workspace_bytes(int B, int L, int H, int Hkv, int d, int num_splits);
+
 /* Split count the library picks for a decode problem (host only; no GPU call).
  * Returns 0 on invalid sizes. */
 int diffattn_decode_num_splits(int B, int L, int Hq, int Hkv, int d);

@@ -190,3 +190,32 @@ def test_backward_workspace_bytes(lib):
     assert bd.diffattn_prefill_bwd_workspace_bytes(2, 100, 8, 2, 64) == (2 * 4 * 5 * 128 + 2 * 2 * 100 * 2 * 64) * 4
     assert bd.diffattn_prefill_bwd_workspace_bytes(1, 100, 6, 2, 64) == 0
     assert bd.diffattn_prefill_bwd_workspace_bytes(0, 100, 8, 2, 64) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=30, Hkv=8), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(H=136, Hkv=8), bd.DIFFATTN_ERR_UNSUPPORTED),     # 17 heads per KV head
+    (dict(d=96), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(L=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(out=P + 8), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(workspace_bytes=64), bd.DIFFATTN_ERR_WORKSPACE),
+])
+def test_compare_decodes_reject(lib, kw, status):
+    a = dict(q=P, k_cache=P, v_cache=P, out=P, B=2, L=100, H=32, Hkv=8, d=128, num_splits=0, workspace=P,
+             workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    assert bd.diffattn_decode_standard(**a) == status
+    a2 = dict(a, lam=P, flags=0, rms_eps=1e-5)
+    assert bd.diffattn_decode_v1_layout(**a2) == status
+
+
+def test_v1_layout_needs_lambda(lib):
+    assert bd.diffattn_decode_v1_layout(P, P, P, None, P, 2, 100, 32, 8, 128, 0, 1e-5, 0, P, 1 << 30,
+                                        None) == bd.DIFFATTN_ERR_INVALID_ARG
+
+
+def test_compare_workspace_bytes(lib):
+    # two record arrays (one per V1 branch) of [B, H, S, d + 4] fp32, S from the decode plan
+    S = bd.diffattn_decode_num_splits(64, 8192, 64, 8, 128)
+    assert bd.diffattn_decode_compare_workspace_bytes(64, 8192, 32, 8, 128, 0) == 2 * 64 * 32 * S * 132 * 4
+    assert bd.diffattn_decode_compare_workspace_bytes(2, 100, 30, 8, 128, 0) == 0
