@@ -9,5 +9,7 @@ from .diffattn_oracle import *  # noqa: F401,F403
 from .diffattn_oracle import __all__ as _fwd_all
 from .diffattn_backward import *  # noqa: F401,F403
 from .diffattn_backward import __all__ as _bwd_all
+from .projections import *  # noqa: F401,F403
+from .projections import __all__ as _proj_all
 
-__all__ = list(_fwd_all) + list(_bwd_all)
+__all__ = list(_fwd_all) + list(_bwd_all) + list(_proj_all)
