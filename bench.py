@@ -89,11 +89,13 @@ def main() -> int:
                     help="untimed wall time of steps before the warmup steps (clock ramp-up); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "serving", "layouts"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "serving", "layouts", "projections"],
+                    default=None,
                     help="time one part (for profiler runs); backward = training forward + backward, "
                          "serving = windowed prefill + ragged decode")
     ap.add_argument("--no-backward", action="store_true", help="skip the training forward / backward timing")
     ap.add_argument("--no-serving", action="store_true", help="skip the serving-variant timing")
+    ap.add_argument("--no-projections", action="store_true", help="skip the lambda producer / O_W timing")
     ap.add_argument("--no-layouts", action="store_true",
                     help="skip the decode layout comparison (standard transformer, DIFF V1, V2)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -133,6 +135,7 @@ def main() -> int:
     do_b = args.only == "backward" or (args.only is None and not args.no_backward)
     do_s = args.only == "serving" or (args.only is None and not args.no_serving)
     do_l = args.only == "layouts" or (args.only is None and not args.no_layouts)
+    do_j = args.only == "projections" or (args.only is None and not args.no_projections)
     if do_p:
         ip = W.make_prefill(wp)
         pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
@@ -320,6 +323,44 @@ def main() -> int:
         layouts["workload"] = (f"B={wd.B} L={wd.T} Hkv={wd.Hkv} d={wd.d} bf16 cache; standard and V1: {H} heads; "
                                f"V2: {wd.Hq} query heads ({wd.P} pairs)")
 
+    projections = None
+    if do_j:
+        # the steps either side of the c2 attention core: lambda for 4096 tokens x 32
+        # pairs from d_model = 4096, and O_W from P*d = 4096 back to d_model = 4096
+        rows, dm, kin = wp.B * wp.T, wp.P * wp.d, wp.P * wp.d
+        ij = W.make_projections(rows, dm, wp.P, kin, dm)
+        jx, jw = dev_bf16(ij["x"]), dev_bf16(ij["w_lambda"])
+        ja, jo = dev_bf16(ij["attn"]), dev_bf16(ij["w_o"])
+        del ij
+        jl = torch.empty((rows, wp.P), dtype=torch.float32, device=dev)
+        jy = torch.empty((rows, dm), dtype=torch.bfloat16, device=dev)
+        jruns = {"lambda_proj": lambda: bd.lambda_proj(jx, jw, out=jl),
+                 "output_proj": lambda: bd.output_proj(ja, jo, out=jy)}
+        jt = {}
+        for name, fn in jruns.items():
+            for _ in range(max(3, args.warmup // 2)):
+                fn()
+            jev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                jev[i][0].record(stream)
+                fn()
+                jev[i][1].record(stream)
+            torch.cuda.synchronize()
+            jt[name] = float(np.mean([e[0].elapsed_time(e[1]) for e in jev]))
+        lp_bytes = rows * dm * 2.0 + wp.P * dm * 2.0 + rows * wp.P * 4.0
+        op_flops = 2.0 * rows * kin * dm
+        projections = {
+            "lambda_proj": {"value": lp_bytes / (jt["lambda_proj"] * 1e-3) / 1e9, "unit": "GB/s",
+                            "ms_per_launch": jt["lambda_proj"], "algorithmic_bytes_per_launch": lp_bytes,
+                            "frac": lp_bytes / (jt["lambda_proj"] * 1e-3) / 1e9 / PEAK_HBM_GBS, "bound": "hbm",
+                            "workload": f"x [{rows}, {dm}] bf16, w [{wp.P}, {dm}] -> lambda [{rows}, {wp.P}] fp32"},
+            "output_proj": {"value": op_flops / (jt["output_proj"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+                            "ms_per_launch": jt["output_proj"], "algorithmic_flops_per_launch": op_flops,
+                            "frac": op_flops / (jt["output_proj"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                            "bound": "mfma", "engine": "rocBLAS gemm_ex (bf16, fp32 accumulate)",
+                            "workload": f"[{rows}, {kin}] x [{kin}, {dm}] bf16"}}
+
     src_p = ["prefill_bf16.hip", "dev_common.h"]
     src_d = ["decode_bf16.hip", "dev_common.h"]
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -347,6 +388,8 @@ def main() -> int:
         res["serving"] = serving
     if layouts is not None:
         res["decode_layouts"] = layouts
+    if projections is not None:
+        res["projections"] = projections
     if bwd is not None:
         res["backward"] = bwd
         if not (do_p or do_d):
@@ -359,7 +402,7 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "decode", "roofline_decode",
-             "backward", "serving", "decode_layouts", "cpu_baseline"]
+             "backward", "serving", "decode_layouts", "projections", "cpu_baseline"]
     print(json.dumps({k: res[k] for k in order if k in res}), flush=True)
     return 0
 

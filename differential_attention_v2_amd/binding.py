@@ -42,6 +42,8 @@ _SIGNATURES = {
     "diffattn_decode_standard": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 6 + [_vp, _c_size, _vp]),
     "diffattn_decode_v1_layout": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_c_uint, _c_float, _c_int, _vp, _c_size, _vp]),
     "diffattn_decode_compare_workspace_bytes": (_c_size, [_c_int] * 6),
+    "diffattn_lambda_proj": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
+    "diffattn_output_proj": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "diffattn_decode_num_splits": (_c_int, [_c_int] * 5),
     "diffattn_decode_workspace_bytes": (_c_size, [_c_int] * 6),
     "diffattn_v1_lambda": (_c_int, [_vp, _vp, _vp, _vp, _c_float, _vp, _c_int, _c_int, _c_int, _vp]),
@@ -126,6 +128,14 @@ def diffattn_decode_v1_layout(q, k_cache, v_cache, lam, out, B, L, H, Hkv, d, fl
 
 def diffattn_decode_compare_workspace_bytes(B, L, H, Hkv, d, num_splits=0):
     return load_library().diffattn_decode_compare_workspace_bytes(B, L, H, Hkv, d, num_splits)
+
+
+def diffattn_lambda_proj(x, w_lambda, lambda_out, rows, d_model, P, stream):
+    return load_library().diffattn_lambda_proj(x, w_lambda, lambda_out, rows, d_model, P, stream)
+
+
+def diffattn_output_proj(attn, w_o, y, rows, in_dim, out_dim, stream):
+    return load_library().diffattn_output_proj(attn, w_o, y, rows, in_dim, out_dim, stream)
 
 
 def diffattn_decode_num_splits(B, L, Hq, Hkv, d):
@@ -295,6 +305,38 @@ def decode_v1_layout(q, k_cache, v_cache, lam, v1_rmsnorm: bool = True, eps: flo
                                    _stream(stream))
     if st != DIFFATTN_OK:
         raise DiffAttnError(st, "diffattn_decode_v1_layout")
+    return out
+
+
+def lambda_proj(x, w_lambda, out=None, stream=None):
+    """lambda [rows, P] fp32 = sigmoid(x [rows, d_model] @ w_lambda [P, d_model]^T), bf16 inputs."""
+    torch = _torch()
+    rows, dm = x.shape
+    P = w_lambda.shape[0]
+    _check(x, "x", (rows, dm), torch.bfloat16)
+    _check(w_lambda, "w_lambda", (P, dm), torch.bfloat16)
+    if out is None:
+        out = torch.empty((rows, P), dtype=torch.float32, device=x.device)
+    _check(out, "out", (rows, P), torch.float32)
+    st = diffattn_lambda_proj(x.data_ptr(), w_lambda.data_ptr(), out.data_ptr(), rows, dm, P, _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_lambda_proj")
+    return out
+
+
+def output_proj(attn, w_o, out=None, stream=None):
+    """y [rows, out_dim] = attn [rows, in_dim] @ w_o [in_dim, out_dim], bf16 (rocBLAS inside the library)."""
+    torch = _torch()
+    rows, kin = attn.shape
+    nout = w_o.shape[1]
+    _check(attn, "attn", (rows, kin), torch.bfloat16)
+    _check(w_o, "w_o", (kin, nout), torch.bfloat16)
+    if out is None:
+        out = torch.empty((rows, nout), dtype=torch.bfloat16, device=attn.device)
+    _check(out, "out", (rows, nout), torch.bfloat16)
+    st = diffattn_output_proj(attn.data_ptr(), w_o.data_ptr(), out.data_ptr(), rows, kin, nout, _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_output_proj")
     return out
 
 

@@ -22,7 +22,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip", "backward_bf16.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip", "backward_bf16.hip", "proj_bf16.hip"]
+# the output projection is a plain GEMM run by rocBLAS
+LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 
 # Packed-fp32 VALU instructions are kept out of every kernel; hipcc -O3 would
 # otherwise form them from plain float code.
@@ -67,7 +69,7 @@ def build(verbose: bool = False, resource_usage: bool = False, jobs: int = 8) ->
     with ThreadPoolExecutor(max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, *LIBS], verbose)
     os.replace(tmp, LIB)
     return LIB
 

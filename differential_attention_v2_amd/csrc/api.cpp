@@ -252,6 +252,26 @@ int diffattn_decode_v1_layout(const void* q, const void* k_cache, const void* v_
                         workspace_bytes, stream);
 }
 
+int diffattn_lambda_proj(const void* x, const void* w_lambda, float* lambda_out, int rows, int d_model, int P,
+                         void* stream) {
+  if (rows < 1 || d_model < 1 || P < 1) return DIFFATTN_ERR_INVALID_ARG;
+  if (d_model % 512 != 0 || P % 16 != 0 || P > 64) return DIFFATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w_lambda, 16) || !aligned(lambda_out, 4)) return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(rows, d_model, 1, 1) || !fits(rows, P, 1, 1)) return DIFFATTN_ERR_INVALID_ARG;
+  return hip_status(launch_lambda_proj(x, w_lambda, lambda_out, rows, d_model, P, static_cast<hipStream_t>(stream)));
+}
+
+int diffattn_output_proj(const void* attn, const void* w_o, void* y, int rows, int in_dim, int out_dim,
+                         void* stream) {
+  if (rows < 1 || in_dim < 1 || out_dim < 1) return DIFFATTN_ERR_INVALID_ARG;
+  if (!aligned(attn, 16) || !aligned(w_o, 16) || !aligned(y, 16)) return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(rows, in_dim, 1, 1) || !fits(in_dim, out_dim, 1, 1) || !fits(rows, out_dim, 1, 1))
+    return DIFFATTN_ERR_INVALID_ARG;
+  return run_output_proj(attn, w_o, y, rows, in_dim, out_dim, static_cast<hipStream_t>(stream)) == 0
+             ? DIFFATTN_OK
+             : DIFFATTN_ERR_HIP;
+}
+
 int diffattn_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2, float lambda_init,
                        float* lambda_out, int P, int d_lambda, int rows, void* stream) {
   if (P < 1 || d_lambda < 1 || rows < 1 || !std::isfinite(lambda_init)) return DIFFATTN_ERR_INVALID_ARG;

@@ -94,6 +94,9 @@ hipError_t launch_prefill_bf16(const PrefillProblem& p, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeProblem& p, hipStream_t s);
 hipError_t launch_backward_bf16(const BackwardProblem& p, hipStream_t s);
 hipError_t launch_decode_compare_bf16(const CompareProblem& p, hipStream_t s);
+hipError_t launch_lambda_proj(const void* x, const void* w, float* lam, int rows, int dm, int P, hipStream_t s);
+// 0 on success
+int run_output_proj(const void* attn, const void* w_o, void* y, int rows, int in_dim, int out_dim, hipStream_t s);
 // fp32 path: rows of queries [B, Tq] over Tk keys; causal limit j <= i + (Tk - Tq).
 hipError_t launch_rows_f32(const PrefillProblem& p, int Tq, int Tk, hipStream_t s);
 hipError_t launch_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,

@@ -205,6 +205,17 @@ def make_compare_decode(B: int, L: int, H: int, Hkv: int, d: int, seed: int) -> 
     return dict(q=q, k=k, v=v, lam=lam)
 
 
+def make_projections(rows: int, d_model: int, P: int, in_dim: int, out_dim: int, seed: int = 6001) -> dict:
+    """Inputs of the projections around the attention core, bf16 bits: x [rows, d_model]
+    ~ N(0, 1), w_lambda [P, d_model] ~ N(0, 1/d_model), attn [rows, in_dim] ~ N(0, 1),
+    w_o [in_dim, out_dim] ~ N(0, 1/in_dim) (unit-variance outputs at initialisation)."""
+    s = _streams(seed)
+    return dict(x=_normal(s[0], rows * d_model, 1.0, "bf16").reshape(rows, d_model),
+                w_lambda=_normal(s[1], P * d_model, 1.0 / math.sqrt(d_model), "bf16").reshape(P, d_model),
+                attn=_normal(s[2], rows * in_dim, 1.0, "bf16").reshape(rows, in_dim),
+                w_o=_normal(s[3], in_dim * out_dim, 1.0 / math.sqrt(in_dim), "bf16").reshape(in_dim, out_dim))
+
+
 def ragged_lengths(B: int, L: int, seed: int = 4242) -> np.ndarray:
     """Per-sequence cache lengths for ragged decode: uniform in [1, L], int32 [B]."""
     return np.random.default_rng(seed).integers(1, L + 1, size=B, dtype=np.int32)

@@ -214,6 +214,31 @@ int diffattn_v1_lambda(const float* lq1, const float* lk1, const float* lq2, con
                        float lambda_init, float* lambda_out, int P, int d_lambda, int rows,
                        void* stream);
 
+/*
+ * lambda producer: V2 projects a sigmoid-bounded lambda for every token and head
+ * (dailytechsnack.ch article, section "Weniger Ausreisser und Gradientenspitzen"):
+ *   lambda_out[r, p] = 1 / (1 + exp(-(x[r] . w_lambda[p])))
+ *   x          device [rows, d_model] bf16 (rows = B*T: the attention block's input)
+ *   w_lambda   device [P, d_model] bf16, one projection vector per pair
+ *   lambda_out device [rows, P] fp32 -- the `lambda` input of the prefill calls
+ * Constraints: d_model % 512 == 0, P % 16 == 0, P <= 64.
+ * Returns a diffattn_status_t.
+ */
+int diffattn_lambda_proj(const void* x, const void* w_lambda, float* lambda_out, int rows, int d_model, int P,
+                         void* stream);
+
+/*
+ * Output projection O_W: the P*d wide differential output projected back to the
+ * model width (differential-attention lesson, section "V1 vs V2").
+ *   y [rows, out_dim] = attn [rows, in_dim] @ w_o [in_dim, out_dim], all bf16
+ *   row-major, fp32 accumulation; attn is the prefill's out viewed as [B*T, P*d].
+ * A plain dense GEMM, run by rocBLAS on `stream`; the library keeps one rocBLAS
+ * handle per calling thread and device (created on first use; rocBLAS may keep
+ * its own device workspace).  Returns a diffattn_status_t.
+ */
+int diffattn_output_proj(const void* attn, const void* w_o, void* y, int rows, int in_dim, int out_dim,
+                         void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* diffattn_status_string(int status);
 

@@ -219,3 +219,23 @@ def test_compare_workspace_bytes(lib):
     S = bd.diffattn_decode_num_splits(64, 8192, 64, 8, 128)
     assert bd.diffattn_decode_compare_workspace_bytes(64, 8192, 32, 8, 128, 0) == 2 * 64 * 32 * S * 132 * 4
     assert bd.diffattn_decode_compare_workspace_bytes(2, 100, 30, 8, 128, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_model=1000), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(P=24), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(P=80), bd.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(rows=0), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(x=P + 8), bd.DIFFATTN_ERR_INVALID_ARG),
+    (dict(lambda_out=None), bd.DIFFATTN_ERR_INVALID_ARG),
+])
+def test_lambda_proj_rejects(lib, kw, status):
+    a = dict(x=P, w_lambda=P, lambda_out=P, rows=16, d_model=4096, P=32, stream=None)
+    a.update(kw)
+    assert bd.diffattn_lambda_proj(**a) == status
+
+
+def test_output_proj_rejects(lib):
+    assert bd.diffattn_output_proj(P, P, None, 16, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
+    assert bd.diffattn_output_proj(P, P + 2, P, 16, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
+    assert bd.diffattn_output_proj(P, P, P, 0, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
