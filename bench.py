@@ -151,6 +151,14 @@ def main() -> int:
         del idc
     stream = torch.cuda.current_stream()
 
+    def settle(fn, ms):
+        """Run fn for `ms` of wall time (untimed) so the clock is at its sustained level."""
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+
     def step(evs=None):
         if do_p:
             if evs: evs[0].record(stream)
@@ -203,11 +211,7 @@ def main() -> int:
             bd.prefill_backward(pq, pk, pv, plam, tout, to2, tlse, bdout, workspace=bws, grads=grads)
             if ev: ev[2].record(stream)
 
-        t0 = time.perf_counter()
-        while (time.perf_counter() - t0) * 1e3 < min(args.settle_ms, 100.0):
-            for _ in range(5):
-                bstep()
-            torch.cuda.synchronize()
+        settle(bstep, min(args.settle_ms, 100.0))
         for _ in range(max(3, args.warmup // 5)):
             bstep()
         bev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -247,14 +251,17 @@ def main() -> int:
         lens_np = W.ragged_lengths(wd.B, wd.T)
         lens = torch.from_numpy(lens_np).to(dev)
         vout = torch.empty((wd.B, wd.P, wd.d), dtype=torch.bfloat16, device=dev)
+        vws = torch.empty(bd.diffattn_decode_varlen_workspace_bytes(wd.B, wd.T, wd.Hq, wd.Hkv, wd.d, 0),
+                          dtype=torch.uint8, device=dev)
 
         def sstep(ev=None):
             if ev: ev[0].record(stream)
             bd.prefill_window(pq, pk, pv, plam, SWA, out=sout)
             if ev: ev[1].record(stream)
-            bd.decode_varlen(dq, dk, dv, dlam, seq_lens=lens, workspace=dws, out=vout)
+            bd.decode_varlen(dq, dk, dv, dlam, seq_lens=lens, workspace=vws, out=vout)
             if ev: ev[2].record(stream)
 
+        settle(sstep, min(args.settle_ms, 100.0))
         for _ in range(max(3, args.warmup // 2)):
             sstep()
         sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -306,6 +313,7 @@ def main() -> int:
         bytes_read = {"standard": 2.0 * cache, "v1_layout": 3.0 * cache, "v2": 2.0 * cache}
         layouts = {}
         for name, fn in runs.items():
+            settle(fn, min(args.settle_ms, 100.0))
             for _ in range(max(3, args.warmup // 2)):
                 fn()
             lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -338,6 +346,7 @@ def main() -> int:
                  "output_proj": lambda: bd.output_proj(ja, jo, out=jy)}
         jt = {}
         for name, fn in jruns.items():
+            settle(fn, min(args.settle_ms, 100.0))
             for _ in range(max(3, args.warmup // 2)):
                 fn()
             jev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]

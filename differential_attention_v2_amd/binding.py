@@ -39,6 +39,7 @@ _SIGNATURES = {
                                             _c_int, _c_int, _vp]),
     "diffattn_prefill_bwd": (_c_int, [_vp] * 12 + [_c_int] * 6 + [_vp, _c_size, _vp]),
     "diffattn_prefill_bwd_workspace_bytes": (_c_size, [_c_int] * 5),
+    "diffattn_decode_varlen_workspace_bytes": (_c_size, [_c_int] * 6),
     "diffattn_decode_standard": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 6 + [_vp, _c_size, _vp]),
     "diffattn_decode_v1_layout": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_c_uint, _c_float, _c_int, _vp, _c_size, _vp]),
     "diffattn_decode_compare_workspace_bytes": (_c_size, [_c_int] * 6),
@@ -112,6 +113,10 @@ def diffattn_prefill_bwd(q, k, v, lam, out, o2, lse, dout, dq, dk, dv, dlam, B, 
 
 def diffattn_prefill_bwd_workspace_bytes(B, T, Hq, Hkv, d):
     return load_library().diffattn_prefill_bwd_workspace_bytes(B, T, Hq, Hkv, d)
+
+
+def diffattn_decode_varlen_workspace_bytes(B, L, Hq, Hkv, d, num_splits=0):
+    return load_library().diffattn_decode_varlen_workspace_bytes(B, L, Hq, Hkv, d, num_splits)
 
 
 def diffattn_decode_standard(q, k_cache, v_cache, out, B, L, H, Hkv, d, num_splits, workspace, workspace_bytes,
@@ -253,7 +258,8 @@ def decode_varlen(q, k_cache, v_cache, lam, seq_lens=None, window: int = 0, v1_r
         out = torch.empty((B, Hq // 2, d), dtype=q.dtype, device=q.device)
     _check(out, "out", (B, Hq // 2, d), q.dtype)
     if workspace is None:
-        workspace = decode_workspace(B, L, Hq, Hkv, d, num_splits, q.device)
+        workspace = torch.empty(diffattn_decode_varlen_workspace_bytes(B, L, Hq, Hkv, d, num_splits),
+                                dtype=torch.uint8, device=q.device)
     st = diffattn_decode_fwd_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lam.data_ptr(),
                                     out.data_ptr(), None if seq_lens is None else seq_lens.data_ptr(), B, L, Hq,
                                     Hkv, d, int(window), DIFFATTN_BF16, DIFFATTN_FLAG_V1_RMSNORM if v1_rmsnorm else 0,

@@ -184,6 +184,24 @@ int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
   return hip_status(launch_decode_bf16(p, s));
 }
 
+namespace {
+// ranges per KV head of the even split over ragged caches: about one wave per SIMD
+int varlen_ranges(int Hkv, int num_splits) {
+  return num_splits > 0 ? num_splits : (kDecodeTargetWaves + Hkv - 1) / Hkv;
+}
+}  // namespace
+
+size_t diffattn_decode_varlen_workspace_bytes(int B, int L, int Hq, int Hkv, int d, int num_splits) {
+  if (check_heads(Hq, Hkv, d) != DIFFATTN_OK || num_splits < 0) return 0;
+  int S, chunk;
+  if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return 0;
+  const size_t split = (size_t)B * Hq * S * decode_record_floats(d) * sizeof(float);
+  const long long ranges = varlen_ranges(Hkv, num_splits);
+  if (ranges * Hkv > kMaxGrid) return 0;
+  const size_t flat = decode_flat_workspace_bytes(B, Hq, d, (int)ranges);
+  return split > flat ? split : flat;
+}
+
 int diffattn_decode_fwd_varlen(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
                                void* out, const int* seq_lens, int B, int L, int Hq, int Hkv, int d, int window,
                                int dtype, unsigned flags, float rms_eps, int num_splits, void* workspace,
@@ -200,12 +218,16 @@ int diffattn_decode_fwd_varlen(const void* q, const void* k_cache, const void* v
   if (!fits(B, L, Hkv, d) || !fits(B, Hq, d, 1)) return DIFFATTN_ERR_INVALID_ARG;
   int S, chunk;
   if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return DIFFATTN_ERR_INVALID_ARG;
-  const size_t need = (size_t)B * Hq * S * decode_record_floats(d) * sizeof(float);
+  const long long ranges = varlen_ranges(Hkv, num_splits);
+  if (ranges * Hkv > kMaxGrid) return DIFFATTN_ERR_INVALID_ARG;
+  const size_t need = seq_lens != nullptr ? decode_flat_workspace_bytes(B, Hq, d, (int)ranges)
+                                          : (size_t)B * Hq * S * decode_record_floats(d) * sizeof(float);
   if (!aligned(workspace, 16) || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
   DecodeProblem p{q, k_cache, v_cache, lambda, out, static_cast<float*>(workspace), B, L, Hq, Hkv, d, S, chunk,
                   (flags & DIFFATTN_FLAG_V1_RMSNORM) ? 1 : 0, rms_eps};
   p.seq_lens = seq_lens;
   p.window = window;
+  p.flat_ranges = seq_lens != nullptr ? (int)ranges : 0;
   return hip_status(launch_decode_bf16(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -51,6 +51,8 @@ struct Args {
   int window;            // visible keys before and including the query, 0 = all
   int nq;                // query heads per KV head served by one wave (<= 16)
   int qoff, koff;        // start of the dot-product slice within q and k rows
+  const int* plan;       // ragged caches: row offsets per sequence, total, rows per range
+  int nslot;             // ragged caches: record slots per query head
 };
 
 // V rows in LDS: row-major [key][d], 16-byte chunks XOR-permuted per row so the
@@ -62,33 +64,23 @@ __device__ __forceinline__ int v_phys(int row, int col) {
   return row * D + ((((col >> 3) ^ sw)) << 3) + (col & 7);
 }
 
+// Attention of the nq query heads of KV head g of sequence b over the cache rows
+// [k0, k1), streamed 32 rows per step.  Writes the partial state of query head
+// n (n < nq) -- unnormalised acc[D], m (log2 domain), l -- to rec0 + n * hstride.
+// vs: this wave's LDS staging for 32 V rows.
 template <int D, int DK>
-__global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
+__device__ __forceinline__ void attend_range(const Args& a, bf16* vs, int b, int g, int k0, int k1, float* rec0,
+                                             size_t hstride) {
   constexpr int KS = DK / 32;                // QK^T k-steps (k = 32 per MFMA)
   constexpr int DB = D / 16;                 // PV d-blocks (16 rows per MFMA)
   constexpr int NCH = D / 8;                 // 16-byte chunks per cache row
   constexpr int VLOADS = KSTEP * NCH / 64;   // V chunks per lane per step
-  __shared__ __attribute__((aligned(16))) bf16 vs[KSTEP * D];
-
   const int lane = threadIdx.x;
   const int n = lane & 15;     // query column = head within the group
   const int grp = lane >> 4;   // 16-lane group
   const int nq = a.nq;
 
-  // KV head fastest: the Hkv waves of one (b, key range) are dispatched together
-  // and stream neighbouring 256-byte pieces of the same cache rows.
-  const int g = blockIdx.x % a.Hkv;
-  const int s = (blockIdx.x / a.Hkv) % a.S;
-  const int b = blockIdx.x / (a.Hkv * a.S);
-  // keys this wave reads: its range of the cache, cut to the sequence's valid
-  // rows [lo, Lb) (lengths outside [1, L] are clamped, so every read stays in
-  // the cache); an empty range leaves m = -inf, l = 0, which the combine skips
-  const int Lb = a.seq_lens ? min(a.L, max(1, a.seq_lens[b])) : a.L;
-  const int lo = a.window > 0 ? max(0, Lb - a.window) : 0;
-  const int k0 = max(s * a.chunk, lo);
-  const int k1 = min(Lb, s * a.chunk + a.chunk);
-
-  // Q^T operand: column n = head g*2G + n, d = 32*ks + 8*grp + 0..7
+  // Q^T operand: column n = head g*nq + n, d = off + 32*ks + 8*grp + 0..7
   bf16x8 qr[KS];
   {
     const bool ok = n < nq;
@@ -188,13 +180,103 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   if (n >= nq) return;
-  const int rec = D + 4;
-  float* w = a.ws + (((size_t)b * a.Hq + g * nq + n) * a.S + s) * rec;
+  float* w = rec0 + n * hstride;
 #pragma unroll
   for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(w + 16 * db + 4 * grp) = o[db];
   if (grp == 0) {
     w[D] = m;
     w[D + 1] = l;
+  }
+}
+
+// One wave per (b, KV head g, key range s); KV head fastest so the Hkv waves of
+// one (b, key range) are dispatched together and stream neighbouring 256-byte
+// pieces of the same cache rows.
+template <int D, int DK>
+__global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) bf16 vs[KSTEP * D];
+  const int g = blockIdx.x % a.Hkv;
+  const int s = (blockIdx.x / a.Hkv) % a.S;
+  const int b = blockIdx.x / (a.Hkv * a.S);
+  // keys this wave reads: its range of the cache, cut to the sequence's valid
+  // rows [lo, Lb) (lengths outside [1, L] are clamped, so every read stays in
+  // the cache); an empty range leaves m = -inf, l = 0, which the combine skips
+  const int Lb = a.seq_lens ? min(a.L, max(1, a.seq_lens[b])) : a.L;
+  const int lo = a.window > 0 ? max(0, Lb - a.window) : 0;
+  const int k0 = max(s * a.chunk, lo);
+  const int k1 = min(Lb, s * a.chunk + a.chunk);
+  const int rec = D + 4;
+  attend_range<D, DK>(a, vs, b, g, k0, k1, a.ws + ((size_t)(b * a.Hq + g * a.nq) * a.S + s) * rec,
+                      (size_t)a.S * rec);
+}
+
+// ---- ragged caches: an even split of the whole batch's valid rows -----------
+// plan[b] = rows of the sequences before b (their windows when a window is
+// set), plan[B] = all rows, plan[B + 1] = rows per range (a multiple of 32).
+__global__ __launch_bounds__(1024) void decode_plan_kernel(const int* seq_lens, int B, int L, int window, int nw,
+                                                           int* plan) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  int carry = 0;
+  for (int c0 = 0; c0 < B; c0 += 1024) {
+    const int b = c0 + t;
+    int len = 0;
+    if (b < B) {
+      const int Lb = min(L, max(1, seq_lens[b]));
+      len = window > 0 ? min(Lb, window) : Lb;
+    }
+    part[t] = len;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {   // inclusive scan
+      const int v = t >= off ? part[t - off] : 0;
+      __syncthreads();
+      part[t] += v;
+      __syncthreads();
+    }
+    if (b < B) plan[b] = carry + part[t] - len;
+    carry += part[1023];
+    __syncthreads();
+  }
+  if (t == 0) {
+    plan[B] = carry;
+    const int per = (carry + nw - 1) / nw;
+    plan[B + 1] = max(32, (per + 31) / 32 * 32);
+  }
+}
+
+// One wave per (range w, KV head g): the rows [w*Kw, (w+1)*Kw) of the batch's
+// concatenated valid rows, one partial record per sequence the range touches,
+// in slot w + b (unique: a later range never reaches back to an earlier sequence).
+template <int D, int DK>
+__global__ __launch_bounds__(64) void decode_flat_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) bf16 vs[KSTEP * D];
+  const int g = blockIdx.x % a.Hkv;
+  const int w = blockIdx.x / a.Hkv;
+  const int* plan = a.plan;
+  const int total = plan[a.B];
+  const int Kw = plan[a.B + 1];
+  int x = w * Kw;
+  const int xend = min(total, x + Kw);
+  if (x >= xend) return;
+  int lo_b = 0, hi_b = a.B - 1;   // last b with plan[b] <= x
+  while (lo_b < hi_b) {
+    const int mid = (lo_b + hi_b + 1) >> 1;
+    if (plan[mid] <= x) lo_b = mid; else hi_b = mid - 1;
+  }
+  int b = lo_b;
+  const int rec = D + 4;
+  const size_t hstride = (size_t)a.nslot * rec;
+  while (x < xend) {
+    const int seg_end = min(xend, plan[b + 1]);
+    if (seg_end > x) {
+      const int Lb = min(a.L, max(1, a.seq_lens[b]));
+      const int lo = a.window > 0 ? max(0, Lb - a.window) : 0;
+      const int k0 = lo + (x - plan[b]);
+      attend_range<D, DK>(a, vs, b, g, k0, k0 + (seg_end - x),
+                          a.ws + ((size_t)(g * a.nq) * a.nslot + w + b) * rec, hstride);
+      x = seg_end;
+    }
+    ++b;
   }
 }
 
@@ -296,6 +378,39 @@ __global__ __launch_bounds__(64) void compare_combine_kernel(Args a, const float
   for (int e = 0; e < E; ++e) dst[e] = (bf16)x[e];
 }
 
+// Ragged caches: one wave per (b, pair); the records of sequence b sit in slots
+// w + b for the ranges w that touch it.
+template <int D>
+__global__ __launch_bounds__(64) void decode_flat_combine_kernel(Args a) {
+  constexpr int E = D / 64;
+  const int bp = blockIdx.x;
+  const int b = bp / a.P, p = bp % a.P;
+  const int lane = threadIdx.x;
+  const int rec = D + 4;
+  const int Kw = a.plan[a.B + 1];
+  const int w0 = a.plan[b] / Kw, w1 = (a.plan[b + 1] - 1) / Kw;
+  float o[2][E];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    merge_head<D>(a.ws + ((size_t)(2 * p + h) * a.nslot + w0 + b) * rec, w1 - w0 + 1, lane, o[h]);
+  const float lamv = a.lam[(size_t)b * a.P + p];
+  float x[E], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = o[0][e] - lamv * o[1][e];
+    ss += x[e] * x[e];
+  }
+  if (a.v1) {
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] *= r;
+  }
+  bf16* dst = a.out + ((size_t)b * a.P + p) * D + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[e] = (bf16)x[e];
+}
+
 template <int D>
 hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
   Args a;
@@ -320,6 +435,20 @@ hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
   a.window = pr.window;
   a.nq = 2 * a.G;
   a.qoff = a.koff = 0;
+  a.plan = nullptr;
+  a.nslot = 0;
+  if (pr.flat_ranges > 0) {   // ragged caches: even split of the batch's valid rows
+    int* plan = reinterpret_cast<int*>(pr.ws + decode_flat_record_floats(pr.B, pr.Hq, pr.d, pr.flat_ranges));
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, pr.seq_lens, pr.B, pr.L, pr.window,
+                       pr.flat_ranges, plan);
+    a.plan = plan;
+    a.nslot = pr.flat_ranges + pr.B;
+    hipLaunchKernelGGL((decode_flat_kernel<D, D>), dim3((unsigned)(pr.flat_ranges * a.Hkv)), dim3(64), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_flat_combine_kernel<D>, dim3((unsigned)(a.B * a.P)), dim3(64), 0, st, a);
+    return hipGetLastError();
+  }
   const long long blocks = (long long)a.B * a.Hkv * a.S;
   hipLaunchKernelGGL((decode_split_kernel<D, D>), dim3((unsigned)blocks), dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();

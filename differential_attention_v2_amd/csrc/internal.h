@@ -36,7 +36,17 @@ struct DecodeProblem {
   float eps;
   const int* seq_lens = nullptr;   // valid cache rows per sequence (device), or null = L
   int window = 0;                  // keys before the query that stay visible, 0 = all
+  int flat_ranges = 0;             // > 0: ragged caches split evenly into this many ranges per KV head
 };
+
+// Ragged-cache decode workspace: records [Hq][ranges + B][d+4] fp32, then the
+// plan: B + 2 ints.
+inline size_t decode_flat_record_floats(int B, int Hq, int d, int ranges) {
+  return (size_t)Hq * (ranges + B) * (d + 4);
+}
+inline size_t decode_flat_workspace_bytes(int B, int Hq, int d, int ranges) {
+  return decode_flat_record_floats(B, Hq, d, ranges) * sizeof(float) + (size_t)(B + 2) * sizeof(int);
+}
 
 // Decode in the layouts V2 is compared against: a standard transformer (H heads,
 // one softmax each) or DIFF V1 (each head's q and k split into halves, one pass

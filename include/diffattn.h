@@ -153,17 +153,23 @@ int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
  * allocated for L (its query is the token at row seq_lens[b]-1), and with
  * window > 0 only its last `window` rows are visible.  Serving engines batch
  * sequences of different lengths this way (the differential-attention lesson,
- * "用它", notes V2 integration into serving engines).
+ * "用它", notes V2 integration into serving engines).  With seq_lens, the
+ * batch's valid rows are split evenly over num_splits ranges per KV head (0 =
+ * library's choice, about one wave per SIMD) by a plan computed on the device,
+ * so long and short sequences cost in proportion to their rows.
  *   seq_lens  device int32 [B], values in [1, L] (values outside are clamped),
- *             or NULL: every sequence has L rows
+ *             or NULL: every sequence has L rows (then as diffattn_decode_fwd)
  *   window    >= 0, 0 = every valid row visible
- *   other arguments as diffattn_decode_fwd (same workspace size); bf16 only
+ *   workspace >= diffattn_decode_varlen_workspace_bytes(...) bytes, 16-byte aligned
+ *   other arguments as diffattn_decode_fwd; bf16 only
  * Returns a diffattn_status_t (fp32 -> DIFFATTN_ERR_UNSUPPORTED).
  */
 int diffattn_decode_fwd_varlen(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
                                void* out, const int* seq_lens, int B, int L, int Hq, int Hkv, int d, int window,
                                int dtype, unsigned flags, float rms_eps, int num_splits, void* workspace,
                                size_t workspace_bytes, void* stream);
+/* Workspace bytes for diffattn_decode_fwd_varlen (host only; 0 on invalid sizes). */
+size_t diffattn_decode_varlen_workspace_bytes(int B, int L, int Hq, int Hkv, int d, int num_splits);
 
 /*
  * Decode in the layouts V2 is measured against (differential-attention lesson,

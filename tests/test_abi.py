@@ -239,3 +239,11 @@ def test_output_proj_rejects(lib):
     assert bd.diffattn_output_proj(P, P, None, 16, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
     assert bd.diffattn_output_proj(P, P + 2, P, 16, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
     assert bd.diffattn_output_proj(P, P, P, 0, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
+
+
+def test_varlen_workspace_bytes(lib):
+    # max of the per-(b, KV head) split records and the even-split records + plan
+    split = 64 * 64 * 2 * 132 * 4
+    flat = 64 * (128 + 64) * 132 * 4 + (64 + 2) * 4
+    assert bd.diffattn_decode_varlen_workspace_bytes(64, 8192, 64, 8, 128, 0) == max(split, flat)
+    assert bd.diffattn_decode_varlen_workspace_bytes(64, 8192, 62, 8, 128, 0) == 0

@@ -100,12 +100,29 @@ def test_decode_varlen_parity(gpu_device, d):
 
 
 def test_decode_varlen_full_lengths_equal_plain_decode(gpu_device):
+    """No lengths: the plain decode, bit for bit.  All lengths = L: the even split
+    over the batch's rows, which partitions the keys differently, agrees closely."""
     w = _decode_case(4, 777, 16, 2, 128, seed=8400)
     _, (q, k, v, lam) = _decode_inputs(w, gpu_device)
-    plain = bd.decode(q, k, v, lam).view(torch.int16)
+    plain = bd.decode(q, k, v, lam)
+    assert torch.equal(bd.decode_varlen(q, k, v, lam).view(torch.int16), plain.view(torch.int16))
     full = torch.full((4,), 777, dtype=torch.int32, device=gpu_device)
-    assert torch.equal(bd.decode_varlen(q, k, v, lam).view(torch.int16), plain)
-    assert torch.equal(bd.decode_varlen(q, k, v, lam, seq_lens=full).view(torch.int16), plain)
+    assert_parity(from_device(bd.decode_varlen(q, k, v, lam, seq_lens=full)), from_device(plain),
+                  "even split, full lengths vs plain decode", max_abs=1e-2, mean_abs=1e-3)
+
+
+def test_decode_varlen_many_short_sequences(gpu_device):
+    """1500 sequences of 1-40 rows: ranges cross many sequences, the plan scans B > 1024."""
+    w = _decode_case(1500, 64, 8, 2, 64, seed=8450)
+    inp, (q, k, v, lam) = _decode_inputs(w, gpu_device)
+    lens_np = np.random.default_rng(8).integers(1, 41, size=1500).astype(np.int32)
+    lens = torch.from_numpy(lens_np).to(gpu_device)
+    f = {n: W.to_f64(inp[n], "bf16") for n in ("q", "k", "v")}
+    for splits in (0, 3):
+        got = from_device(bd.decode_varlen(q, k, v, lam, seq_lens=lens, num_splits=splits))
+        sel = np.arange(0, 1500, 37)
+        ref = oracle.diffattn_decode(f["q"], f["k"], f["v"], inp["lam"], batches=sel, seq_lens=lens_np)
+        assert_parity(got[sel], ref, f"1500 short sequences splits={splits}")
 
 
 def test_decode_varlen_clamps_out_of_range_lengths(gpu_device):
