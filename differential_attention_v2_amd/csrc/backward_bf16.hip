@@ -47,13 +47,20 @@ constexpr int NF = kBackwardFields;   // row-statistics fields: lse2_1, lse2_2, 
 
 // ---------------------------------------------------------------------------
 // LDS tile layout shared by every tile here: unpadded row-major [row][d], the
-// 16-byte chunks of a row XOR-permuted by (row mod NCH).  Row reads (ds_read_b128
-// of 32 rows at one chunk) and transposing reads (4 rows x 16 columns per 16
-// lanes) both stay within a few banks' conflicts.
+// 16-byte chunks of a row XOR-permuted by swz(row), which swaps the two low bit
+// fields of the row index: ((row % 4) << 2) | (row / 4 % 4) for 16 chunks per row
+// (((row % 4) << 1) | (row / 4 % 2) for 8).  It is a bijection on 16 (8)
+// consecutive rows, so a row read (ds_read_b128 of consecutive rows at one
+// chunk) spreads over all chunks, and for 4 consecutive rows it differs in its
+// upper bits, so a transposing read (4 rows x 2 chunks per 16 lanes) touches 8
+// distinct chunks.  Rows 16 apart share the permutation.
+template <int D>
+__device__ __forceinline__ int t_swz(int row) {
+  return D >= 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : (((row & 3) << 1) | ((row >> 2) & 1));
+}
 template <int D>
 __device__ __forceinline__ int t_phys(int row, int col) {
-  constexpr int NCH = D / 8;
-  return row * D + ((((col >> 3) ^ (row & (NCH - 1)))) << 3) + (col & 7);
+  return row * D + ((((col >> 3) ^ t_swz<D>(row))) << 3) + (col & 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -226,8 +233,8 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
     const int slot = (j * A_WAVES + wave) * 64 + lane;
     const int r = slot / NCH, pc = slot % NCH;
     srow[j] = r;
-    qofs[j] = r * qrow + 16 * (pc ^ (r & (NCH - 1)));
-    dofs[j] = r * drow + 16 * (pc ^ (r & (NCH - 1)));
+    qofs[j] = r * qrow + 16 * (pc ^ t_swz<D>(r));
+    dofs[j] = r * drow + 16 * (pc ^ t_swz<D>(r));
   }
   // row statistics: 5 fields x 32 tokens = 40 chunks of 16 bytes; lanes past
   // them repeat the last chunk into the unused tail of the slot
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
     const int slot = (j * B_WAVES + wave) * 64 + lane;
     const int r = slot / NCH, pc = slot % NCH;
     drow[j] = r;
-    dofs[j] = r * row_bytes + 16 * (pc ^ (r & (NCH - 1)));
+    dofs[j] = r * row_bytes + 16 * (pc ^ t_swz<D>(r));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)LDS_PTR(const char, lds);
   auto dma_tile = [&](int t, int buf) {
