@@ -292,16 +292,42 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
     if (a.causal && t0 + A_QT - 1 < kw0) return;   // every key of this wave is in the future
     if (kw0 >= T) return;
     // S_1, S_2 = Q_r K^T and dP = dout V^T: rows (tokens) x this wave's keys
+    // (A operands read one k-step ahead of their products)
     f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
+    auto load_a = [&](int s, bf16x8 (&o)[3]) {
+#pragma unroll
+      for (int m = 0; m < 3; ++m) o[m] = *reinterpret_cast<const bf16x8*>(sb + m * TILE + aofs[s]);
+    };
+    bf16x8 aop[2][3];
+    load_a(0, aop[0]);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(sb + aofs[s]);
-      const bf16x8 q2 = *reinterpret_cast<const bf16x8*>(sb + TILE + aofs[s]);
-      const bf16x8 go = *reinterpret_cast<const bf16x8*>(sb + 2 * TILE + aofs[s]);
-      s1 = mfma32(q1, kreg[s], s1);
-      s2 = mfma32(q2, kreg[s], s2);
-      dp = mfma32(go, vreg[s], dp);
+      if (s + 1 < KSTEPS) load_a(s + 1, aop[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      s1 = mfma32(aop[s & 1][0], kreg[s], s1);
+      s2 = mfma32(aop[s & 1][1], kreg[s], s2);
+      dp = mfma32(aop[s & 1][2], vreg[s], dp);
     }
+    // B operands of the dV / dK products (dout, Q_1, Q_2 read transposed), for
+    // iteration it = (ks, db); read one iteration ahead of the products that use
+    // them, the first before the softmax arithmetic, so that LDS latency hides
+    // behind MFMA and VALU work
+    constexpr int NIT = 2 * DBLK;
+    auto load_b = [&](int it, bf16x8 (&o)[3]) {
+      const int ks = it / DBLK, db = it % DBLK;
+      const int ro = 16 * ks * D * 2;
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        const int tile = m == 0 ? 2 : m - 1;
+        const char* p0 = sb + tile * TILE + tofs[db][0] + ro;
+        const char* p1 = sb + tile * TILE + tofs[db][1] + ro;
+        o[m] = concat(lds_read_tr4(reinterpret_cast<const bf16*>(p0)),
+                      lds_read_tr4(reinterpret_cast<const bf16*>(p1)));
+      }
+    };
+    bf16x8 bop[2][3];
+    load_b(0, bop[0]);
+    __builtin_amdgcn_sched_barrier(0);
     // lane holds rows 8 (i/4) + 4 hi + i%4 of the tile for key l32
     const bool need_mask = (a.causal && t0 < kw0 + 31) || t0 + A_QT > T || kw0 + 32 > T;
     bf16x8 pc[2], d1[2], d2[2];
@@ -335,20 +361,14 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
     }
     // dV += (P_1 - lambda P_2)^T dout,  dK += dS_1^T Q_1 + dS_2^T Q_2
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int ro = 16 * ks * D * 2;
-        auto tr = [&](int tile) {
-          const char* p0 = sb + tile * TILE + tofs[db][0] + ro;
-          const char* p1 = sb + tile * TILE + tofs[db][1] + ro;
-          return concat(lds_read_tr4(reinterpret_cast<const bf16*>(p0)),
-                        lds_read_tr4(reinterpret_cast<const bf16*>(p1)));
-        };
-        dv[db] = mfma32(pc[ks], tr(2), dv[db]);
-        dk[db] = mfma32(d1[ks], tr(0), dk[db]);
-        dk[db] = mfma32(d2[ks], tr(1), dk[db]);
-      }
+    for (int it = 0; it < NIT; ++it) {
+      if (it + 1 < NIT) load_b(it + 1, bop[(it + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int ks = it / DBLK, db = it % DBLK;
+      dv[db] = mfma32(pc[ks], bop[it & 1][0], dv[db]);
+      dk[db] = mfma32(d1[ks], bop[it & 1][1], dk[db]);
+      dk[db] = mfma32(d2[ks], bop[it & 1][2], dk[db]);
+    }
   };
 
   // ---- staging ring: step j uses stage j % 3; the copy for step j+2 goes into
