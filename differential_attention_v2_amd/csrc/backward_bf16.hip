@@ -154,7 +154,7 @@ struct GradArgs {
   int nkb;            // key blocks per (b, g)
   int nqt;            // 32-token query tiles
   int qtc;            // query tiles per chunk
-  int nchunk;         // chunks per key block (upper bound)
+  int nchunk;         // query chunks
   // dQ grid (the forward's decomposition)
   int ppw, nsub, chunks, ntb, units;
 };
@@ -164,7 +164,18 @@ constexpr int A_WAVES = 4;
 constexpr int A_THREADS = 64 * A_WAVES;
 constexpr int A_KBLK = 32 * A_WAVES;   // keys per workgroup
 constexpr int A_QT = 32;               // query tokens per tile
-constexpr int A_NS = 3;                // staging ring depth
+constexpr int A_NS = 3;                // staging ring depth (3 or 4)
+static_assert(A_NS == 3 || A_NS == 4, "staging ring depth");
+constexpr int PF_A = 1;                // k-steps the S-phase operand reads run ahead
+constexpr int PF_B = 1;                // iterations the dV/dK operand reads run ahead
+
+// Key blocks paired with query chunk c: those whose first key is at or before
+// the chunk's last token (every key block without the causal mask).
+__host__ __device__ inline int chunk_key_blocks(const GradArgs& a, int c) {
+  if (!a.causal) return a.nkb;
+  const int last_tile = min(a.nqt, (c + 1) * a.qtc) - 1;
+  return min(a.nkb, last_tile * A_QT / A_KBLK + 1);
+}
 
 template <int D>
 __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
@@ -186,20 +197,30 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
   const int hi = lane >> 5;
   const int T = a.T;
 
-  // ---- workgroup -> ((b, g), key block, query chunk); chunk-major so that the
-  // full chunks (nearest the diagonal) start first
+  // ---- workgroup -> ((b, g), query chunk, key block).  Chunks are fixed ranges
+  // of qtc query tiles; chunk c pairs with every key block that has a visible
+  // key in it (all of them without the causal mask).  Workgroups run from the
+  // last chunk down, key blocks in order, so the workgroups that run together on
+  // one XCD (same (b, g): blockIdx % units) stream the same query tiles and share
+  // them through L2.
   const int units = a.B * a.Hkv;
   const int u = blockIdx.x % units;
-  const int rest = blockIdx.x / units;
-  const int kb = rest % a.nkb;
-  const int ch = rest / a.nkb;
+  int idx = blockIdx.x / units;
+  int qc = a.nchunk - 1;
+  for (; qc >= 0; --qc) {
+    const int n = chunk_key_blocks(a, qc);
+    if (idx < n) break;
+    idx -= n;
+  }
+  if (qc < 0) return;
+  const int kb = idx;
   const int g = u % a.Hkv;
   const int b = u / a.Hkv;
   const int k0 = kb * A_KBLK;
   const int qt_first = a.causal ? k0 / A_QT : 0;
-  const int qt0 = qt_first + ch * a.qtc;
-  if (qt0 >= a.nqt) return;   // whole workgroup: empty chunk
-  const int qt1 = min(a.nqt, qt0 + a.qtc);
+  const int qt0 = max(qc * a.qtc, qt_first);
+  const int qt1 = min(a.nqt, (qc + 1) * a.qtc);
+  if (qt0 >= qt1) return;
   const int nsteps = (qt1 - qt0) * a.G;
 
   // ---- this wave's 32 keys: K and V rows as the B operands of Q K^T and dout V^T
@@ -298,15 +319,16 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
 #pragma unroll
       for (int m = 0; m < 3; ++m) o[m] = *reinterpret_cast<const bf16x8*>(sb + m * TILE + aofs[s]);
     };
-    bf16x8 aop[2][3];
-    load_a(0, aop[0]);
+    bf16x8 aop[PF_A + 1][3];
+#pragma unroll
+    for (int s = 0; s < PF_A; ++s) load_a(s, aop[s]);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      if (s + 1 < KSTEPS) load_a(s + 1, aop[(s + 1) & 1]);
+      if (s + PF_A < KSTEPS) load_a(s + PF_A, aop[(s + PF_A) % (PF_A + 1)]);
       __builtin_amdgcn_sched_barrier(0);
-      s1 = mfma32(aop[s & 1][0], kreg[s], s1);
-      s2 = mfma32(aop[s & 1][1], kreg[s], s2);
-      dp = mfma32(aop[s & 1][2], vreg[s], dp);
+      s1 = mfma32(aop[s % (PF_A + 1)][0], kreg[s], s1);
+      s2 = mfma32(aop[s % (PF_A + 1)][1], kreg[s], s2);
+      dp = mfma32(aop[s % (PF_A + 1)][2], vreg[s], dp);
     }
     // B operands of the dV / dK products (dout, Q_1, Q_2 read transposed), for
     // iteration it = (ks, db); read one iteration ahead of the products that use
@@ -325,8 +347,9 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
                       lds_read_tr4(reinterpret_cast<const bf16*>(p1)));
       }
     };
-    bf16x8 bop[2][3];
-    load_b(0, bop[0]);
+    bf16x8 bop[PF_B + 1][3];
+#pragma unroll
+    for (int it = 0; it < PF_B; ++it) load_b(it, bop[it]);
     __builtin_amdgcn_sched_barrier(0);
     // lane holds rows 8 (i/4) + 4 hi + i%4 of the tile for key l32
     const bool need_mask = (a.causal && t0 < kw0 + 31) || t0 + A_QT > T || kw0 + 32 > T;
@@ -362,27 +385,32 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
     // dV += (P_1 - lambda P_2)^T dout,  dK += dS_1^T Q_1 + dS_2^T Q_2
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      if (it + 1 < NIT) load_b(it + 1, bop[(it + 1) & 1]);
+      if (it + PF_B < NIT) load_b(it + PF_B, bop[(it + PF_B) % (PF_B + 1)]);
       __builtin_amdgcn_sched_barrier(0);
       const int ks = it / DBLK, db = it % DBLK;
-      dv[db] = mfma32(pc[ks], bop[it & 1][0], dv[db]);
-      dk[db] = mfma32(d1[ks], bop[it & 1][1], dk[db]);
-      dk[db] = mfma32(d2[ks], bop[it & 1][2], dk[db]);
+      dv[db] = mfma32(pc[ks], bop[it % (PF_B + 1)][0], dv[db]);
+      dk[db] = mfma32(d1[ks], bop[it % (PF_B + 1)][1], dk[db]);
+      dk[db] = mfma32(d2[ks], bop[it % (PF_B + 1)][2], dk[db]);
     }
   };
 
-  // ---- staging ring: step j uses stage j % 3; the copy for step j+2 goes into
-  // the stage of step j-1, which every wave finished before the barrier that
-  // closed step j-1
-  stage_copy(0, 0);
-  if (nsteps > 1) stage_copy(1, 1);
+  // ---- staging ring: step j uses stage j % A_NS; the copy for step j+A_NS-1
+  // goes into the stage of step j-1, which every wave finished before the
+  // barrier that closed step j-1.  After step j the copy for step j+1 must have
+  // landed; the later ones may stay in flight.
+#pragma unroll
+  for (int j = 0; j < A_NS - 1; ++j)
+    if (j < nsteps) stage_copy(j, j);
   wait_vmcnt0_builtin();
   __syncthreads();
   auto one = [&](int j, auto st_c) {
     constexpr int ST = decltype(st_c)::value;
-    if (j + 2 < nsteps) stage_copy(j + 2, (ST + 2) % A_NS);
+    if (j + A_NS - 1 < nsteps) stage_copy(j + A_NS - 1, (ST + A_NS - 1) % A_NS);
     compute(j, st_c);
-    if (j + 2 < nsteps)
+    const int ahead = min(A_NS - 2, nsteps - 2 - j);   // copies allowed in flight
+    if (A_NS > 3 && ahead >= 2)
+      wait_vmcnt<2 * LOADS>();
+    else if (ahead >= 1)
       wait_vmcnt<LOADS>();
     else
       wait_vmcnt<0>();
@@ -392,6 +420,8 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
     one(j, std::integral_constant<int, 0>{});
     if (j + 1 < nsteps) one(j + 1, std::integral_constant<int, 1>{});
     if (j + 2 < nsteps) one(j + 2, std::integral_constant<int, 2>{});
+    if constexpr (A_NS > 3)
+      if (j + 3 < nsteps) one(j + 3, std::integral_constant<int, 3 % A_NS>{});
   }
 
   // ---- add this chunk's share to the fp32 accumulators.  C layout: lane l,
@@ -663,7 +693,9 @@ hipError_t launch(const BackwardProblem& pr, hipStream_t s) {
   a.ntb = (pr.T + B_QT * a.nsub - 1) / (B_QT * a.nsub);
   a.units = pr.B * pr.Hkv * a.chunks;
 
-  const long long ga = (long long)pr.B * pr.Hkv * a.nkb * a.nchunk;
+  long long pairs = 0;   // (chunk, key block) pairs per (b, g)
+  for (int c = 0; c < a.nchunk; ++c) pairs += chunk_key_blocks(a, c);
+  const long long ga = (long long)pr.B * pr.Hkv * pairs;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)ga), dim3(A_THREADS), 0, s, a);
   const long long gb = (long long)a.ntb * a.units;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gb), dim3(B_THREADS), 0, s, a);
