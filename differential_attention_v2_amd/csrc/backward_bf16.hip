@@ -351,12 +351,22 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
 #pragma unroll
     for (int it = 0; it < PF_B; ++it) load_b(it, bop[it]);
     __builtin_amdgcn_sched_barrier(0);
-    // lane holds rows 8 (i/4) + 4 hi + i%4 of the tile for key l32
-    const bool need_mask = (a.causal && t0 < kw0 + 31) || t0 + A_QT > T || kw0 + 32 > T;
+    // lane holds rows 8 (i/4) + 4 hi + i%4 of the tile for key l32.  Hidden
+    // entries (future keys, rows or keys past T) get score -inf, so their P and dS
+    // come out exactly 0 from the common arithmetic below; only tiles on the
+    // diagonal or at the sequence end take this branch.
+    if ((a.causal && t0 < kw0 + 31) || t0 + A_QT > T || kw0 + 32 > T) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = t0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        const bool vis = tok < T && key < T && (!a.causal || key <= tok);
+        s1[i] = vis ? s1[i] : -INFINITY;
+        s2[i] = vis ? s2[i] : -INFINITY;
+      }
+    }
     bf16x8 pc[2], d1[2], d2[2];
     const float* rsl = reinterpret_cast<const float*>(sb + 3 * TILE);
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
+    auto grad_group = [&](int gq) {
       const int r0 = 8 * gq + 4 * hi;
       const f32x4 L1 = *reinterpret_cast<const f32x4*>(rsl + 0 * A_QT + r0);
       const f32x4 L2 = *reinterpret_cast<const f32x4*>(rsl + 1 * A_QT + r0);
@@ -366,14 +376,8 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * gq + e;
-        float p1 = fast_exp2(__builtin_fmaf(s1[i], c, -L1[e]));
-        float p2 = fast_exp2(__builtin_fmaf(s2[i], c, -L2[e]));
-        if (need_mask) {
-          const int tok = t0 + r0 + e;
-          const bool vis = tok < T && key < T && (!a.causal || key <= tok);
-          p1 = vis ? p1 : 0.f;
-          p2 = vis ? p2 : 0.f;
-        }
+        const float p1 = fast_exp2(__builtin_fmaf(s1[i], c, -L1[e]));
+        const float p2 = fast_exp2(__builtin_fmaf(s2[i], c, -L2[e]));
         const float x1 = p1 * (dp[i] - D1[e]);
         const float x2 = -p2 * __builtin_fmaf(LM[e], dp[i], D2[e]);
         const float xc = __builtin_fmaf(-LM[e], p2, p1);
@@ -381,7 +385,9 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
         d1[i >> 3][i & 7] = (bf16)x1;
         d2[i >> 3][i & 7] = (bf16)x2;
       }
-    }
+    };
+    grad_group(0);
+    grad_group(1);
     // dV += (P_1 - lambda P_2)^T dout,  dK += dS_1^T Q_1 + dS_2^T Q_2
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -391,6 +397,7 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
       dv[db] = mfma32(pc[ks], bop[it % (PF_B + 1)][0], dv[db]);
       dk[db] = mfma32(d1[ks], bop[it % (PF_B + 1)][1], dk[db]);
       dk[db] = mfma32(d2[ks], bop[it % (PF_B + 1)][2], dk[db]);
+      if (it < 2) grad_group(2 + it);   // rows 16..31 issue while the ks = 0 products run
     }
   };
 
