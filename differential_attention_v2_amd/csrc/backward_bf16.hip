@@ -580,36 +580,51 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
       const int ro = kb * 32 * D * 2;
       // S^T = K Q^T and dP^T = V dout^T (keys x rows)
       f32x16 st = f32x16{}, dpt = f32x16{};
+      bf16x8 kva[2][2];
+      auto load_kv = [&](int s, bf16x8 (&o)[2]) {
+        o[0] = *reinterpret_cast<const bf16x8*>(lds + KO + ro + aofs[s]);
+        o[1] = *reinterpret_cast<const bf16x8*>(lds + VO + ro + aofs[s]);
+      };
+      load_kv(0, kva[0]);
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lds + KO + ro + aofs[s]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(lds + VO + ro + aofs[s]);
-        st = mfma32(ka, qreg[s], st);
-        dpt = mfma32(va, oreg[s], dpt);
+        if (s + 1 < KSTEPS) load_kv(s + 1, kva[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        st = mfma32(kva[s & 1][0], qreg[s], st);
+        dpt = mfma32(kva[s & 1][1], oreg[s], dpt);
       }
-      const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T;
+      // hidden keys (future, or past T) get score -inf: P and dS come out 0
+      if ((a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const bool vis = key < T && (!a.causal || key <= qtok);
+          st[i] = vis ? st[i] : -INFINITY;
+        }
+      }
       bf16x8 ds[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(__builtin_fmaf(st[i], c, -L2));
-        if (need_mask) {
-          const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          const bool vis = key < T && (!a.causal || key <= qtok);
-          pv = vis ? pv : 0.f;
-        }
+        const float pv = fast_exp2(__builtin_fmaf(st[i], c, -L2));
         ds[i >> 3][i & 7] = (bf16)(pv * __builtin_fmaf(sr, dpt[i], -Dr));
       }
-      // dQ^T += K^T dS^T
+      // dQ^T += K^T dS^T (K^T operands read one product ahead)
+      constexpr int NIT = 2 * DBLK;
+      auto load_kt = [&](int it) {
+        const int ks = it / DBLK, db = it % DBLK;
+        const char* p0 = lds + KO + ro + 16 * ks * D * 2 + tofs[db][0];
+        const char* p1 = lds + KO + ro + 16 * ks * D * 2 + tofs[db][1];
+        return concat(lds_read_tr4(reinterpret_cast<const bf16*>(p0)),
+                      lds_read_tr4(reinterpret_cast<const bf16*>(p1)));
+      };
+      bf16x8 kt[2];
+      kt[0] = load_kt(0);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const char* p0 = lds + KO + ro + 16 * ks * D * 2 + tofs[db][0];
-          const char* p1 = lds + KO + ro + 16 * ks * D * 2 + tofs[db][1];
-          const bf16x8 kt = concat(lds_read_tr4(reinterpret_cast<const bf16*>(p0)),
-                                   lds_read_tr4(reinterpret_cast<const bf16*>(p1)));
-          o[db] = mfma32(kt, ds[ks], o[db]);
-        }
+      for (int it = 0; it < NIT; ++it) {
+        if (it + 1 < NIT) kt[(it + 1) & 1] = load_kt(it + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        o[it % DBLK] = mfma32(kt[it & 1], ds[it / DBLK], o[it % DBLK]);
+      }
     }
   };
 
