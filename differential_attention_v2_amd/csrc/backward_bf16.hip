@@ -265,29 +265,44 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
     rsofs = (uint32_t)((cidx / 8) * a.Tpad * 4 + 16 * (cidx % 8));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)LDS_PTR(const char, smem);
-  auto stage_copy = [&](int step, int st) {
-    const int tq = qt0 + step / a.G;
-    const int p = g * a.G + step % a.G;
-    const int t0 = tq * A_QT;
-    const char* qb = reinterpret_cast<const char*>(a.q) + (((size_t)b * T + t0) * a.Hq + 2 * p) * D * 2;
-    const char* db = reinterpret_cast<const char*>(a.dout) + (((size_t)b * T + t0) * a.P + p) * D * 2;
-    const char* rb = reinterpret_cast<const char*>(a.rs) + (((size_t)b * a.P + p) * NF * a.Tpad + t0) * 4;
-    const bool tail = t0 + A_QT > T;
+  // Copy cursor: the (query tile, pair) of the next step to stage and its three
+  // source rows, advanced by constant strides (steps run pair-fastest), so no
+  // step recomputes a 64-bit address.
+  int cp_t0 = qt0 * A_QT, cp_pp = 0;
+  const char* cp_q = reinterpret_cast<const char*>(a.q) + (((size_t)b * T + cp_t0) * a.Hq + 2 * g * a.G) * D * 2;
+  const char* cp_d = reinterpret_cast<const char*>(a.dout) + (((size_t)b * T + cp_t0) * a.P + g * a.G) * D * 2;
+  const char* cp_r = reinterpret_cast<const char*>(a.rs) + (((size_t)b * a.P + g * a.G) * NF * a.Tpad + cp_t0) * 4;
+  const long long rs_pair = (long long)NF * a.Tpad * 4;
+  const long long q_tile = (long long)A_QT * a.Hq * D * 2 - (long long)a.G * 4 * D;
+  const long long d_tile = (long long)A_QT * a.P * D * 2 - (long long)a.G * 2 * D;
+  const long long r_tile = (long long)A_QT * 4 - a.G * rs_pair;
+  auto stage_copy = [&](int st) {
+    const bool tail = cp_t0 + A_QT > T;
     const uint32_t sbase = lds_base + st * STAGE;
 #pragma unroll
     for (int j = 0; j < TLOADS; ++j) {
       uint32_t oq = qofs[j], od = dofs[j];
       if (tail) {
-        const int back = max(0, t0 + srow[j] - (T - 1));
+        const int back = max(0, cp_t0 + srow[j] - (T - 1));
         oq -= back * qrow;
         od -= back * drow;
       }
       const uint32_t dst = sbase + (j * A_WAVES + wave) * 1024;
-      dma16_saddr(qb, oq, dst);
-      dma16_saddr(qb + D * 2, oq, dst + TILE);
-      dma16_saddr(db, od, dst + 2 * TILE);
+      dma16_saddr(cp_q, oq, dst);
+      dma16_saddr(cp_q + D * 2, oq, dst + TILE);
+      dma16_saddr(cp_d, od, dst + 2 * TILE);
     }
-    dma16_saddr(rb, rsofs, sbase + 3 * TILE + wave * 1024);
+    dma16_saddr(cp_r, rsofs, sbase + 3 * TILE + wave * 1024);
+    cp_q += 4 * D;
+    cp_d += 2 * D;
+    cp_r += rs_pair;
+    if (++cp_pp == a.G) {
+      cp_pp = 0;
+      cp_t0 += A_QT;
+      cp_q += q_tile;
+      cp_d += d_tile;
+      cp_r += r_tile;
+    }
   };
 
   // ---- per-lane LDS read offsets (bytes within a tile)
@@ -306,10 +321,9 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
 
   const float c = a.scale_log2;
 
-  auto compute = [&](int step, auto st_c) {
+  auto compute = [&](int t0, auto st_c) {
     constexpr int ST = decltype(st_c)::value;
     const char* sb = smem + ST * STAGE;
-    const int t0 = (qt0 + step / a.G) * A_QT;
     if (a.causal && t0 + A_QT - 1 < kw0) return;   // every key of this wave is in the future
     if (kw0 >= T) return;
     // S_1, S_2 = Q_r K^T and dP = dout V^T: rows (tokens) x this wave's keys
@@ -407,13 +421,18 @@ __global__ __launch_bounds__(A_THREADS, 1) void bwd_dkdv_kernel(GradArgs a) {
   // landed; the later ones may stay in flight.
 #pragma unroll
   for (int j = 0; j < A_NS - 1; ++j)
-    if (j < nsteps) stage_copy(j, j);
+    if (j < nsteps) stage_copy(j);
   wait_vmcnt0_builtin();
   __syncthreads();
+  int ct0 = qt0 * A_QT, cpp = 0;   // compute cursor: query tile and pair of step j
   auto one = [&](int j, auto st_c) {
     constexpr int ST = decltype(st_c)::value;
-    if (j + A_NS - 1 < nsteps) stage_copy(j + A_NS - 1, (ST + A_NS - 1) % A_NS);
-    compute(j, st_c);
+    if (j + A_NS - 1 < nsteps) stage_copy((ST + A_NS - 1) % A_NS);
+    compute(ct0, st_c);
+    if (++cpp == a.G) {
+      cpp = 0;
+      ct0 += A_QT;
+    }
     const int ahead = min(A_NS - 2, nsteps - 2 - j);   // copies allowed in flight
     if (A_NS > 3 && ahead >= 2)
       wait_vmcnt<2 * LOADS>();
