@@ -15,7 +15,7 @@ from _helpers import assert_parity, from_device, to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("rows,dm,P", [(4096, 4096, 32), (100, 512, 16), (37, 1024, 64)])
+@pytest.mark.parametrize("rows,dm,P", [(4096, 4096, 32), (100, 512, 16), (37, 1024, 64), (50, 1536, 48), (16, 8192, 32)])
 def test_lambda_projection(gpu_device, rows, dm, P):
     inp = W.make_projections(rows, dm, P, 512, 512, seed=6100 + rows)
     x, w = to_device(inp["x"], "bf16", gpu_device), to_device(inp["w_lambda"], "bf16", gpu_device)
