@@ -320,10 +320,10 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   // proves that every wave finished tile t-1, whose buffer then receives tile
   // t+3.
   dma_tile(t_first, 0);
+  wait_vmcnt0_builtin();   // Q operands and the first tile have landed
+  __syncthreads();
   if (nt > 1) dma_tile(t_first + 1, 1);
   if (nt > 2) dma_tile(t_first + 2, 2);
-  wait_vmcnt0_builtin();   // Q operands and the first tiles have landed
-  __syncthreads();
   load_k(0);
   // ring position r holds tile t_first + r in buffer r % NBUF
   auto tile = [&](int r, auto bufc) {
