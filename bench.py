@@ -89,13 +89,15 @@ def main() -> int:
                     help="untimed wall time of steps before the warmup steps (clock ramp-up); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "serving", "layouts", "projections"],
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "serving", "layouts", "projections", "long"],
                     default=None,
                     help="time one part (for profiler runs); backward = training forward + backward, "
                          "serving = windowed prefill + ragged decode")
     ap.add_argument("--no-backward", action="store_true", help="skip the training forward / backward timing")
     ap.add_argument("--no-serving", action="store_true", help="skip the serving-variant timing")
     ap.add_argument("--no-projections", action="store_true", help="skip the lambda producer / O_W timing")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long configurations (T=32768 prefill, B=8 L=131072 decode)")
     ap.add_argument("--no-layouts", action="store_true",
                     help="skip the decode layout comparison (standard transformer, DIFF V1, V2)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -136,6 +138,7 @@ def main() -> int:
     do_s = args.only == "serving" or (args.only is None and not args.no_serving)
     do_l = args.only == "layouts" or (args.only is None and not args.no_layouts)
     do_j = args.only == "projections" or (args.only is None and not args.no_projections)
+    do_g = args.only == "long" or (args.only is None and not args.no_long)
     if do_p:
         ip = W.make_prefill(wp)
         pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
@@ -370,6 +373,71 @@ def main() -> int:
                             "bound": "mfma", "engine": "rocBLAS gemm_ex (bf16, fp32 accumulate)",
                             "workload": f"[{rows}, {kin}] x [{kin}, {dm}] bf16"}}
 
+    long_cfg = None
+    if do_g:
+        # the long configurations, timed only (their parity runs in the GPU tests):
+        # T=32768 causal prefill and the B=8, L=131072 decode, V2 and V1 mode.
+        # Inputs are drawn on the device from a seeded generator with the same
+        # distributions as the host generator (host generation of 4.3 GB of cache
+        # would take minutes).
+        w3, w5 = W.CONFIGS[3], W.CONFIGS[5]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(3000 + 3)
+
+        def rnd(shape, scale=1.0):
+            return (torch.randn(shape, generator=gen, device=dev, dtype=torch.bfloat16) * scale).contiguous()
+
+        lq = rnd((w3.B, w3.T, w3.Hq, w3.d), 0.7071)
+        lk = rnd((w3.B, w3.T, w3.Hkv, w3.d), 0.7071)
+        lv = rnd((w3.B, w3.T, w3.Hkv, w3.d), 0.7071)
+        llam = torch.sigmoid(torch.randn((w3.B, w3.T, w3.P), generator=gen, device=dev))
+        lout = torch.empty((w3.B, w3.T, w3.P, w3.d), dtype=torch.bfloat16, device=dev)
+
+        def time_fn(fn, steps):
+            for _ in range(2):
+                fn()
+            lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            torch.cuda.synchronize()
+            for i in range(steps):
+                lev[i][0].record(stream)
+                fn()
+                lev[i][1].record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([e[0].elapsed_time(e[1]) for e in lev]))
+
+        lsteps = max(3, min(args.steps, 10))
+        settle(lambda: bd.prefill(lq, lk, lv, llam, out=lout), min(args.settle_ms, 100.0))
+        ms3 = time_fn(lambda: bd.prefill(lq, lk, lv, llam, out=lout), lsteps)
+        del lq, lk, lv, llam, lout
+        gen.manual_seed(3000 + 5)
+        cq = rnd((w5.B, w5.Hq, w5.d))
+        ck = rnd((w5.B, w5.T, w5.Hkv, w5.d))
+        cv = rnd((w5.B, w5.T, w5.Hkv, w5.d))
+        clam = torch.sigmoid(torch.randn((w5.B, w5.P), generator=gen, device=dev))
+        cout5 = torch.empty((w5.B, w5.P, w5.d), dtype=torch.bfloat16, device=dev)
+        cws = bd.decode_workspace(w5.B, w5.T, w5.Hq, w5.Hkv, w5.d, 0, dev)
+        settle(lambda: bd.decode(cq, ck, cv, clam, workspace=cws, out=cout5), min(args.settle_ms, 100.0))
+        ms5 = time_fn(lambda: bd.decode(cq, ck, cv, clam, workspace=cws, out=cout5), args.steps)
+        ms5v1 = time_fn(lambda: bd.decode(cq, ck, cv, clam, v1_rmsnorm=True, eps=1e-5, workspace=cws, out=cout5),
+                        args.steps)
+        del cq, ck, cv, clam, cout5, cws
+        f3, b5 = w3.prefill_flops(), w5.decode_kv_bytes()
+        long_cfg = {
+            "prefill": {"value": f3 / (ms3 * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_launch": ms3,
+                        "frac": f3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "algorithmic_flops_per_launch": f3,
+                        "traffic": _traffic("prefill_long"),
+                        "workload": f"{w3.name}: B={w3.B} T={w3.T} Hq={w3.Hq} Hkv={w3.Hkv} d={w3.d} causal bf16"},
+            "decode": {"value": b5 / (ms5 * 1e-3) / 1e9, "unit": "GB/s", "ms_per_launch": ms5,
+                       "frac": b5 / (ms5 * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": b5,
+                       "traffic": _traffic("decode_long"),
+                       "splits": bd.diffattn_decode_num_splits(w5.B, w5.T, w5.Hq, w5.Hkv, w5.d),
+                       "workload": f"{w5.name}: B={w5.B} L={w5.T} Hq={w5.Hq} Hkv={w5.Hkv} d={w5.d} bf16"},
+            "decode_v1_mode": {"value": b5 / (ms5v1 * 1e-3) / 1e9, "unit": "GB/s", "ms_per_launch": ms5v1,
+                               "frac": b5 / (ms5v1 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               "workload": f"{w5.name}, V1 reference mode (RMSNorm after the difference)"},
+            "inputs": "drawn on the device: torch bf16 normals (q, k, v scaled 1/sqrt(2) for the prefill), "
+                      "lambda = sigmoid(N(0,1)), seeded"}
+
     src_p = ["prefill_bf16.hip", "dev_common.h"]
     src_d = ["decode_bf16.hip", "dev_common.h"]
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -399,6 +467,8 @@ def main() -> int:
         res["decode_layouts"] = layouts
     if projections is not None:
         res["projections"] = projections
+    if long_cfg is not None:
+        res["long_configs"] = long_cfg
     if bwd is not None:
         res["backward"] = bwd
         if not (do_p or do_d):
@@ -411,7 +481,7 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "decode", "roofline_decode",
-             "backward", "serving", "decode_layouts", "projections", "cpu_baseline"]
+             "backward", "serving", "decode_layouts", "projections", "long_configs", "cpu_baseline"]
     print(json.dumps({k: res[k] for k in order if k in res}), flush=True)
     return 0
 
