@@ -4,6 +4,11 @@
     python -m differential_attention_v2_amd.rocprof_summary stats DIR/run_kernel_stats.csv \
         --cmd "<the rocprofv3 command>" --title "..." --out profiles/NAME.txt
 
+    # MFMA utilisation and effective shader clock from one counter run of
+    # GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA
+    python -m differential_attention_v2_amd.rocprof_summary util DIR/run_counter_collection.csv \
+        --cmd "..." --title "..." --out profiles/NAME.txt
+
     # HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE runs, scaled by what the
     # same counters read for a plain device copy of known size
     python -m differential_attention_v2_amd.rocprof_summary traffic \
@@ -112,6 +117,42 @@ def cmd_traffic(a) -> None:
     print("\n".join(lines))
 
 
+XCDS = 8      # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+
+
+def cmd_util(a) -> None:
+    """Per kernel (medians over dispatches): duration, effective shader clock
+    (GRBM_GUI_ACTIVE per XCD / duration) and MFMA busy share of all SIMD cycles."""
+    per = {}
+    for r in csv.DictReader(open(a.csv)):
+        d = per.setdefault(_short(r["Kernel_Name"]), {})
+        key = (r["Dispatch_Id"])
+        rec = d.setdefault(key, {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+        rec[r["Counter_Name"]] = float(r["Counter_Value"])
+    lines = [f"# {a.title}", "", "command:", f"  {a.cmd}", "",
+             f"{'kernel':44s} {'dispatches':>10s} {'dur_us':>9s} {'sclk_GHz':>9s} {'mfma_busy%':>10s} "
+             f"{'mfma_insts':>12s}"]
+    for k, recs in per.items():
+        if any(k.startswith(pre) for pre in a.skip):
+            continue
+        ok = [x for x in recs.values() if "GRBM_GUI_ACTIVE" in x and x["dur"] > 0]
+        if not ok:
+            continue
+        dur = statistics.median(x["dur"] for x in ok)
+        clk = statistics.median(x["GRBM_GUI_ACTIVE"] / XCDS / x["dur"] for x in ok) / 1e9
+        busy = [x["SQ_VALU_MFMA_BUSY_CYCLES"] / (x["GRBM_GUI_ACTIVE"] / XCDS * SIMDS) * 100
+                for x in ok if "SQ_VALU_MFMA_BUSY_CYCLES" in x]
+        insts = [x["SQ_INSTS_MFMA"] for x in ok if "SQ_INSTS_MFMA" in x]
+        lines.append(f"{k[:44]:44s} {len(ok):10d} {dur * 1e6:9.1f} {clk:9.3f} "
+                     f"{(statistics.median(busy) if busy else float('nan')):10.1f} "
+                     f"{(statistics.median(insts) if insts else float('nan')):12.0f}")
+    if a.note:
+        lines += ["", a.note]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -123,6 +164,13 @@ def main(argv=None) -> int:
     s.add_argument("--trace", default=None, help="run_kernel_trace.csv, for the mean of the last dispatches")
     s.add_argument("--last", type=int, default=20)
     s.add_argument("--out", required=True)
+    u = sub.add_parser("util")
+    u.add_argument("csv")
+    u.add_argument("--cmd", required=True)
+    u.add_argument("--title", required=True)
+    u.add_argument("--note", default="")
+    u.add_argument("--out", required=True)
+    u.add_argument("--skip", action="append", default=[], help="kernel-name prefix to leave out (repeatable)")
     t = sub.add_parser("traffic")
     for n in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + n.replace("_", "-"), dest=n, required=True)
@@ -134,7 +182,7 @@ def main(argv=None) -> int:
     t.add_argument("--out", required=True)
     t.add_argument("--json", default=None)
     a = ap.parse_args(argv)
-    cmd_stats(a) if a.what == "stats" else cmd_traffic(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "util": cmd_util}[a.what](a)
     return 0
 
 
