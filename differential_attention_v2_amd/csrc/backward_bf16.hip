@@ -20,14 +20,16 @@
 //   fill:      zero the fp32 dK/dV accumulators.
 //   bwd_dkdv:  key-block outer.  A workgroup of 4 waves owns 128 keys of one
 //              (b, g) (32 keys per wave, K and V held in registers as MFMA
-//              operands) and a chunk of query tokens; for every 32-token query
-//              tile and every pair of the group, Q_1, Q_2 and dout tiles (and the
-//              row statistics) are staged in LDS by direct global-to-LDS loads
-//              and read by all 4 waves.  Scores are computed as S = Q K^T
-//              (lanes own keys), so P and dS feed the dV and dK products straight
-//              from registers; the row-major Q and dout tiles are transposed by
-//              the LDS transpose read.  Results are added to fp32 accumulators
-//              (query chunks of one key block run in different workgroups).
+//              operands) and one fixed 512-token chunk of queries; for every
+//              32-token query tile and every pair of the group, Q_1, Q_2 and
+//              dout tiles (and the row statistics) are staged in LDS by direct
+//              global-to-LDS loads and read by all 4 waves.  Scores are computed
+//              as S = Q K^T (lanes own keys), so P and dS feed the dV and dK
+//              products straight from registers; the row-major Q and dout tiles
+//              are transposed by the LDS transpose read.  Hidden scores are set
+//              to -inf once per step, MFMA operands are read one product group
+//              ahead.  Results are added to fp32 accumulators (the query chunks
+//              of one key block run in different workgroups).
 //   bwd_dq:    query-block outer, the forward's structure: 8 waves, each one
 //              pair x 16 tokens (its 32 rows are the MFMA columns), K/V tiles
 //              streamed through a 4-deep LDS ring shared by the whole group.
