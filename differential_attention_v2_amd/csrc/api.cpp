@@ -309,7 +309,7 @@ const char* diffattn_status_string(int status) {
     case DIFFATTN_OK: return "ok";
     case DIFFATTN_ERR_INVALID_ARG: return "invalid argument";
     case DIFFATTN_ERR_UNSUPPORTED: return "unsupported configuration";
-    case DIFFATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case DIFFATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case DIFFATTN_ERR_HIP: return "HIP runtime or kernel launch failure";
     default: return "unknown status";
   }

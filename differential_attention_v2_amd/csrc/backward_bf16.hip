@@ -699,14 +699,6 @@ hipError_t launch(const BackwardProblem& pr, hipStream_t s) {
   float* dv_acc = dk_acc + (size_t)pr.B * pr.T * pr.Hkv * D;
   const long long nkv = (long long)pr.B * pr.T * pr.Hkv * D;
 
-  PreArgs pa{static_cast<const bf16*>(pr.out), static_cast<const bf16*>(pr.o2), static_cast<const bf16*>(pr.dout),
-             pr.lam, pr.lse, rs, pr.dlam, pr.B, pr.T, P, Tpad};
-  {
-    const long long threads = (long long)pr.B * Tpad * P * (D / 8);
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, pa);
-  }
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(2048), dim3(256), 0, s, reinterpret_cast<float4*>(dk_acc), 2 * nkv / 4);
-
   GradArgs a;
   a.q = static_cast<const bf16*>(pr.q);
   a.k = static_cast<const bf16*>(pr.k);
@@ -736,11 +728,20 @@ hipError_t launch(const BackwardProblem& pr, hipStream_t s) {
   a.ntb = (pr.T + B_QT * a.nsub - 1) / (B_QT * a.nsub);
   a.units = pr.B * pr.Hkv * a.chunks;
 
+  // grid sizes, checked before anything is enqueued: the dK/dV grid grows with T^2
   long long pairs = 0;   // (chunk, key block) pairs per (b, g)
   for (int c = 0; c < a.nchunk; ++c) pairs += chunk_key_blocks(a, c);
   const long long ga = (long long)pr.B * pr.Hkv * pairs;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)ga), dim3(A_THREADS), 0, s, a);
   const long long gb = (long long)a.ntb * a.units;
+  const long long gpre = ((long long)pr.B * Tpad * P * (D / 8) + 255) / 256;
+  constexpr long long kMaxGrid = (1LL << 31) - 1;
+  if (ga > kMaxGrid || gb > kMaxGrid || gpre > kMaxGrid) return hipErrorInvalidConfiguration;
+
+  PreArgs pa{static_cast<const bf16*>(pr.out), static_cast<const bf16*>(pr.o2), static_cast<const bf16*>(pr.dout),
+             pr.lam, pr.lse, rs, pr.dlam, pr.B, pr.T, P, Tpad};
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)gpre), dim3(256), 0, s, pa);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(2048), dim3(256), 0, s, reinterpret_cast<float4*>(dk_acc), 2 * nkv / 4);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)ga), dim3(A_THREADS), 0, s, a);
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gb), dim3(B_THREADS), 0, s, a);
   hipLaunchKernelGGL(convert_kernel, dim3(2048), dim3(256), 0, s, reinterpret_cast<const float4*>(dk_acc),
                      static_cast<bf16x4*>(pr.dk), nkv / 4);

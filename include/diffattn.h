@@ -49,7 +49,7 @@ typedef enum {
   DIFFATTN_OK = 0,
   DIFFATTN_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, non-positive size, bad ratio, overflow */
   DIFFATTN_ERR_UNSUPPORTED = 2, /* valid but not built: head dim, group size, dtype */
-  DIFFATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  DIFFATTN_ERR_WORKSPACE = 3,   /* workspace missing or too small */
   DIFFATTN_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } diffattn_status_t;
 
@@ -116,7 +116,8 @@ int diffattn_prefill_fwd_train(const void* q, const void* k, const void* v, cons
  * Outputs are fully overwritten and must not alias any input.  dk and dv are
  * summed over query chunks with fp32 atomics, so their last bits can vary from
  * run to run; dq and dlambda are deterministic.
- * Returns a diffattn_status_t.
+ * Returns a diffattn_status_t; sizes whose dK/dV grid (growing with T^2) would
+ * exceed 2^31-1 workgroups return DIFFATTN_ERR_HIP with nothing enqueued.
  */
 int diffattn_prefill_bwd(const void* q, const void* k, const void* v, const float* lambda, const void* out,
                          const void* o2, const float* lse, const void* dout, void* dq, void* dk, void* dv,
