@@ -37,10 +37,21 @@
 namespace diffattn {
 namespace {
 
-constexpr int BN = 64;           // keys per LDS tile
 constexpr int QT = 16;           // query tokens per wave (x 2 heads = 32 MFMA columns)
-constexpr int WAVES = 8;
-constexpr int THREADS = 64 * WAVES;
+// Two tile shapes of one kernel.  SHAPE 0 (full prefill): 8 waves (two per SIMD),
+// 64-key tiles in a 4-deep ring, a barrier in the middle of each tile.  SHAPE 1
+// (sliding window): 4 waves, 32-key tiles in a 5-deep ring (80 KB), so two
+// workgroups share a CU and their waves interleave on each SIMD without a common
+// barrier; a window gives each workgroup only ~17 64-key tiles, and the second
+// workgroup then hides the first one's prologue and tail (+7 % measured), while
+// for full prefill the doubled tile staging makes it 2 % slower.
+template <int SHAPE> struct Shape {
+  static constexpr int WAVES = SHAPE == 0 ? 8 : 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BN = SHAPE == 0 ? 64 : 32;     // keys per LDS tile
+  static constexpr int NBUF = SHAPE == 0 ? 4 : 5;     // ring depth
+  static constexpr int WG_PER_CU = SHAPE == 0 ? 1 : 2;
+};
 constexpr float SUM_LIMIT = 65536.0f;  // per-lane half-tile row-sum bound (2^16)
 
 struct Args {
@@ -85,18 +96,22 @@ __device__ __forceinline__ float max16(const f32x16& x) {
   return fmaxf(m, x[15]);
 }
 
-template <int D>
-__global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
+template <int D, int SHAPE>
+__global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) void prefill_kernel(Args a) {
+  constexpr int WAVES = Shape<SHAPE>::WAVES;
+  constexpr int THREADS = Shape<SHAPE>::THREADS;
+  constexpr int BN = Shape<SHAPE>::BN;
+  constexpr int HPT = BN / 32;             // 32-key half tiles per tile
   constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // QK^T k-steps
   constexpr int DBLK = D / 32;             // PV output d-blocks
   constexpr int LOADS = BN * NCH / THREADS;  // 16-byte chunks per thread per tile (K or V)
   static_assert(LOADS >= 1 && (BN * NCH) % THREADS == 0, "tile/thread mismatch");
-  // K/V tiles in a 4-deep ring: tile t lives in buffer t % NBUF and is requested
-  // three tiles ahead of its use, so its copy overlaps three tiles of compute.
+  // K/V tiles in a ring: tile t lives in buffer t % NBUF and is requested
+  // NBUF-1 tiles ahead of its use, so its copy overlaps several tiles of compute.
   // The NBUF K buffers come first, then the NBUF V buffers, so every operand read
-  // is a per-lane offset plus a compile-time immediate below 64 KB.
-  constexpr int NBUF = 4;
+  // is a per-lane offset plus a compile-time immediate below 80 KB.
+  constexpr int NBUF = Shape<SHAPE>::NBUF;
   constexpr int TILE_BYTES = BN * D * 2;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * NBUF * BN * D];
   const char* lds = reinterpret_cast<const char*>(smem);
@@ -244,13 +259,13 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
     for (int s = 0; s < KSTEPS; ++s) ka[s] = *reinterpret_cast<const bf16x8*>(lds + kofs[s] + off);
   };
 
-  // half tile h = 2t + KB, held in ring buffer BUF
+  // half tile h = HPT t + KB, held in ring buffer BUF
   auto half = [&](int t, auto kb_c, auto buf_c) {
     constexpr int KB = decltype(kb_c)::value;
     constexpr int BUF = decltype(buf_c)::value;
     // LDS offset of the K half tile that follows this one
-    constexpr int KNEXT = KB == 0 ? BUF * TILE_BYTES + 32 * D * 2 : ((BUF + 1) % NBUF) * TILE_BYTES;
-    const int h = 2 * t + KB;
+    constexpr int KNEXT = KB + 1 < HPT ? BUF * TILE_BYTES + (KB + 1) * 32 * D * 2 : ((BUF + 1) % NBUF) * TILE_BYTES;
+    const int h = HPT * t + KB;
     if (h + 1 == h_first) load_k(KNEXT);   // the wave's first K operands
     if (h < h_first || h > hl) return;
     const int kbase_tok = 32 * h;
@@ -313,36 +328,44 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
       for (int db = 0; db < DBLK; ++db) o[db] = mfma32(va[ks][db], pp[ks], o[db]);
   };
 
-  // ---- tile loop, unrolled by NBUF so each buffer index is a constant.  Tile t
-  // is read from the second half of tile t-1 (its first K half, read ahead) to
-  // its own second half.  The barrier between the two halves of tile t
-  // publishes tile t+1 (each wave waited for its own share of the copy) and
-  // proves that every wave finished tile t-1, whose buffer then receives tile
-  // t+3.
+  // ---- tile loop, unrolled by NBUF so each buffer index is a constant.
+  // SHAPE 0: tile t is read from the second half of tile t-1 (its first K half,
+  // read ahead) to its own second half.  The barrier between the two halves of
+  // tile t publishes tile t+1 (each wave waited for its own share of the copy)
+  // and proves that every wave finished tile t-1, whose buffer then receives tile
+  // t+3.  SHAPE 1: during tile t the waves read tiles t and t+1 (K one tile
+  // ahead); the barrier after tile t publishes tile t+2 and proves every wave
+  // finished tile t, so tile t+4 goes into the buffer of tile t-1.
+  constexpr int FIRST = SHAPE == 0 ? 1 : 2;   // tiles published before the loop
   dma_tile(t_first, 0);
-  wait_vmcnt0_builtin();   // Q operands and the first tile have landed
+  if (FIRST > 1 && nt > 1) dma_tile(t_first + 1, 1);
+  wait_vmcnt0_builtin();   // Q operands and the first tiles have landed
   __syncthreads();
-  if (nt > 1) dma_tile(t_first + 1, 1);
-  if (nt > 2) dma_tile(t_first + 2, 2);
+#pragma unroll
+  for (int j = FIRST; j < NBUF - 1; ++j)
+    if (j < nt) dma_tile(t_first + j, j);
   load_k(0);
   // ring position r holds tile t_first + r in buffer r % NBUF
   auto tile = [&](int r, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     const int t = t_first + r;
     half(t, std::integral_constant<int, 0>{}, bufc);
-    if (r + 2 < nt)
+    // the next tile to publish must have landed; one later copy may stay in flight
+    if (r + NBUF - 2 < nt)
       wait_vmcnt<2 * LOADS>();
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (r + 3 < nt) dma_tile(t + 3, (BUF + 3) % NBUF);
-    half(t, std::integral_constant<int, 1>{}, bufc);
+    if (r + NBUF - 1 < nt) dma_tile(t + NBUF - 1, (BUF + NBUF - 1) % NBUF);
+    if constexpr (HPT > 1) half(t, std::integral_constant<int, 1>{}, bufc);
   };
   for (int r = 0; r < nt; r += NBUF) {
     tile(r, std::integral_constant<int, 0>{});
     if (r + 1 < nt) tile(r + 1, std::integral_constant<int, 1>{});
     if (r + 2 < nt) tile(r + 2, std::integral_constant<int, 2>{});
     if (r + 3 < nt) tile(r + 3, std::integral_constant<int, 3>{});
+    if constexpr (NBUF > 4)
+      if (r + 4 < nt) tile(r + 4, std::integral_constant<int, 4 % NBUF>{});
   }
 
   if (!active) return;
@@ -395,8 +418,9 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_kernel(Args a) {
   if (ok) store_rows(a.out);
 }
 
-template <int D>
+template <int D, int SHAPE>
 hipError_t launch(const PrefillProblem& pr, hipStream_t s) {
+  constexpr int WAVES = Shape<SHAPE>::WAVES;
   Args a;
   a.q = static_cast<const bf16*>(pr.q);
   a.k = static_cast<const bf16*>(pr.k);
@@ -423,14 +447,16 @@ hipError_t launch(const PrefillProblem& pr, hipStream_t s) {
   a.ntb = (a.T + tokens_wg - 1) / tokens_wg;
   a.units = a.B * a.Hkv * a.chunks;
   const long long blocks = (long long)a.ntb * a.units;
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)blocks), dim3(THREADS), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<D, SHAPE>), dim3((unsigned)blocks), dim3(Shape<SHAPE>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillProblem& p, hipStream_t s) {
-  return p.d == 128 ? launch<128>(p, s) : launch<64>(p, s);
+  const bool window = p.causal && p.window > 0;
+  if (p.d == 128) return window ? launch<128, 1>(p, s) : launch<128, 0>(p, s);
+  return window ? launch<64, 1>(p, s) : launch<64, 0>(p, s);
 }
 
 }  // namespace diffattn
