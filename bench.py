@@ -279,6 +279,7 @@ def main() -> int:
             "prefill_window": {"value": wp.prefill_flops(SWA) / (ms_sw * 1e-3) / 1e12, "unit": "TFLOP/s",
                                "ms_per_launch": ms_sw, "window": SWA,
                                "algorithmic_flops_per_launch": wp.prefill_flops(SWA),
+                               "kernel": "prefill_kernel<128, 1>", "traffic": _traffic("prefill_window"),
                                "frac": wp.prefill_flops(SWA) / (ms_sw * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                "workload": f"{wp.name} causal, window {SWA}"},
             "decode_varlen": {"value": vl_bytes / (ms_vl * 1e-3) / 1e9, "unit": "GB/s", "ms_per_launch": ms_vl,
@@ -448,7 +449,7 @@ def main() -> int:
         res.update(value=tflops, unit="TFLOP/s")
         res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tflops / PEAK_BF16_TFLOPS, "traffic": _traffic("prefill"),
-                           "kernel": "prefill_kernel<128>", "ms_per_launch": ms_pre,
+                           "kernel": "prefill_kernel<128, 0>", "ms_per_launch": ms_pre,
                            "algorithmic_flops_per_launch": wp.prefill_flops()}
     if do_d:
         gbs = wd.decode_kv_bytes() / (ms_dec * 1e-3) / 1e9
@@ -457,7 +458,7 @@ def main() -> int:
                          "splits": bd.diffattn_decode_num_splits(wd.B, wd.T, wd.Hq, wd.Hkv, wd.d)}
         res["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": gbs / PEAK_HBM_GBS, "traffic": _traffic("decode"),
-                                  "kernel": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                                  "kernel": "decode_split_kernel<128, 128> + decode_combine_kernel<128>",
                                   "algorithmic_bytes_per_launch": wd.decode_kv_bytes()}
         if not do_p:
             res.update(value=gbs, unit="GB/s")
