@@ -9,14 +9,18 @@
 // per step and raises decode arithmetic intensity).
 //
 // Split kernel: one wave per (b, KV head g, key range s).  It streams its key
-// range once, 32 keys per step, with 16-byte loads (16 lanes cover one 256-byte
-// cache row), and computes the scores of the group's 2G query heads at once on
-// v_mfma_f32_16x16x32_bf16 (A = 16 cache keys straight from the loads, B = the
-// 2G query heads, padded to 16 columns).  P^T stays in registers as the B operand
-// of O^T += V^T P^T; the V^T operand is read from a row-major copy of the V rows
-// in LDS with the transposing LDS read.  Each wave writes, per query head, its
-// partial softmax state (running max m in the log2 domain, denominator l and the
-// unnormalised accumulator) to the workspace.
+// range once, 32 keys per step: the step's K and V rows are copied global -> LDS
+// directly (global_load_lds, nontemporal), each instruction moving whole 256-byte
+// rows, one step ahead of the step being computed (two LDS stages).  Loading the
+// K operand straight into registers would touch 16 rows x 64 bytes per
+// instruction, which streams measurably slower than whole rows.  The scores of
+// the group's 2G query heads are computed at once on v_mfma_f32_16x16x32_bf16
+// (A = 16 cache keys read from LDS, B = the 2G query heads, padded to 16
+// columns).  P^T stays in registers as the B operand of O^T += V^T P^T; the V^T
+// operand comes from the row-major V rows in LDS with the transposing LDS read.
+// Each wave writes, per query head, its partial softmax state (running max m in
+// the log2 domain, denominator l and the unnormalised accumulator) to the
+// workspace.
 //
 // Combine kernel: one wave per (b, pair).  For both heads of the pair it
 // merges the partial states (M = max_s m_s, weights 2^(m_s - M)), normalises,
@@ -64,17 +68,51 @@ __device__ __forceinline__ int v_phys(int row, int col) {
   return row * D + ((((col >> 3) ^ sw)) << 3) + (col & 7);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane with the nontemporal hint (the
+// cache is read exactly once): scalar base, per-lane byte offset, lane l's bytes
+// land at lds_addr + 16 l.  Inline asm, so the compiler adds no waits of its own;
+// the caller waits on vmcnt before reading the stage.
+__device__ __forceinline__ void dma16_stream(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  // one wait state between the M0 write and the copy that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds_addr), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
+// K-slice rows in LDS: [key][DK], 16-byte chunks XOR-permuted so that the MFMA
+// operand reads (16 rows x one chunk per 16-lane group) hit distinct banks.
+template <int KCH>
+__device__ __forceinline__ int k_swz(int row) {
+  constexpr int SH = KCH >= 16 ? 0 : (KCH == 8 ? 1 : 2);
+  return (row >> SH) & (KCH - 1);
+}
+
+// LDS per wave: two stages of (32 K-slice rows, 32 V rows)
+template <int D, int DK>
+struct DecodeLds {
+  static constexpr int KBYTES = KSTEP * DK * 2;
+  static constexpr int VBYTES = KSTEP * D * 2;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int BYTES = 2 * STAGE;
+};
+
 // Attention of the nq query heads of KV head g of sequence b over the cache rows
 // [k0, k1), streamed 32 rows per step.  Writes the partial state of query head
 // n (n < nq) -- unnormalised acc[D], m (log2 domain), l -- to rec0 + n * hstride.
-// vs: this wave's LDS staging for 32 V rows.
+// Each step's K slice and V rows are copied global -> LDS directly, four or more
+// whole rows per instruction, one step ahead of the one being computed; lds is
+// this wave's DecodeLds<D, DK>::BYTES.
 template <int D, int DK>
-__device__ __forceinline__ void attend_range(const Args& a, bf16* vs, int b, int g, int k0, int k1, float* rec0,
+__device__ __forceinline__ void attend_range(const Args& a, char* lds, int b, int g, int k0, int k1, float* rec0,
                                              size_t hstride) {
-  constexpr int KS = DK / 32;                // QK^T k-steps (k = 32 per MFMA)
-  constexpr int DB = D / 16;                 // PV d-blocks (16 rows per MFMA)
-  constexpr int NCH = D / 8;                 // 16-byte chunks per cache row
-  constexpr int VLOADS = KSTEP * NCH / 64;   // V chunks per lane per step
+  using LD = DecodeLds<D, DK>;
+  constexpr int KS = DK / 32;                  // QK^T k-steps (k = 32 per MFMA)
+  constexpr int DB = D / 16;                   // PV d-blocks (16 rows per MFMA)
+  constexpr int NCH = D / 8;                   // 16-byte chunks per V row
+  constexpr int KCH = DK / 8;                  // 16-byte chunks per K-slice row
+  constexpr int KLOADS = KSTEP * KCH / 64;     // copy instructions per step
+  constexpr int VLOADS = KSTEP * NCH / 64;
+  constexpr int LOADS = KLOADS + VLOADS;
   const int lane = threadIdx.x;
   const int n = lane & 15;     // query column = head within the group
   const int grp = lane >> 4;   // 16-lane group
@@ -90,42 +128,77 @@ __device__ __forceinline__ void attend_range(const Args& a, bf16* vs, int b, int
       u32x4 x = ok ? ldg16(src + 32 * ks) : u32x4{0, 0, 0, 0};
       qr[ks] = __builtin_bit_cast(bf16x8, x);
     }
+    // q arrives before the first cache copy is issued: the compiler then has no
+    // load of its own outstanding in the loop and inserts no wait there
+    wait_vmcnt0_builtin();
   }
-  const size_t row = (size_t)a.Hkv * D;
-  const bf16* kb0 = a.k + ((size_t)b * a.L * a.Hkv + g) * D;
-  const bf16* vb0 = a.v + ((size_t)b * a.L * a.Hkv + g) * D;
+  const uint32_t row_bytes = (uint32_t)a.Hkv * D * 2;
+  const char* kb0 = reinterpret_cast<const char*>(a.k + ((size_t)b * a.L * a.Hkv + g) * D);
+  const char* vb0 = reinterpret_cast<const char*>(a.v + ((size_t)b * a.L * a.Hkv + g) * D);
   const float c = a.scale_log2;
+
+  // copy instruction j, lane l fills LDS slot 64 j + l of the K (or V) stage:
+  // row slot / CH, physical chunk slot % CH = logical chunk ^ swizzle(row)
+  uint32_t kofs[KLOADS], vofs[VLOADS];
+  int krow[KLOADS], vrow[VLOADS];
+#pragma unroll
+  for (int j = 0; j < KLOADS; ++j) {
+    const int r = (64 * j + lane) / KCH, pc = lane % KCH;
+    krow[j] = r;
+    kofs[j] = r * row_bytes + 2 * a.koff + 16 * (pc ^ k_swz<KCH>(r));
+  }
+#pragma unroll
+  for (int j = 0; j < VLOADS; ++j) {
+    const int r = (64 * j + lane) / NCH, pc = lane % NCH;
+    vrow[j] = r;
+    vofs[j] = r * row_bytes + 2 * (v_phys<D>(r, 8 * pc) - r * D);   // v_phys permutes chunks within the row
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)LDS_PTR(const char, lds);
+  // rows past k1 (last step only) repeat row k1 - 1: finite data, masked out
+  auto issue = [&](int kk, int st) {
+    const char* kt = kb0 + (size_t)kk * row_bytes;
+    const char* vt = vb0 + (size_t)kk * row_bytes;
+    const int last = k1 - 1 - kk;
+    const uint32_t dst = lds_base + st * LD::STAGE;
+#pragma unroll
+    for (int j = 0; j < KLOADS; ++j)
+      dma16_stream(kt, kofs[j] - (uint32_t)max(0, krow[j] - last) * row_bytes, dst + 1024 * j);
+#pragma unroll
+    for (int j = 0; j < VLOADS; ++j)
+      dma16_stream(vt, vofs[j] - (uint32_t)max(0, vrow[j] - last) * row_bytes, dst + LD::KBYTES + 1024 * j);
+  };
+
+  // per-lane LDS read offsets: K operand of k-step ks for keys 16 h + n
+  uint32_t krd[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) krd[ks] = n * DK * 2 + 16 * ((4 * ks + grp) ^ k_swz<KCH>(n));
 
   f32x4 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x4{};
   float m = -INFINITY, l = 0.f;
 
-  for (int kk = k0; kk < k1; kk += KSTEP) {
-    // ---- issue all loads of this step: K as MFMA A operands, V rows for LDS
-    u32x4 ka[2][KS];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = kk + 16 * h + n;
-      const bool ok = key < k1;
-      const bf16* src = kb0 + (size_t)(ok ? key : k0) * row + a.koff + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ka[h][ks] = ok ? ldg16_stream(src + 32 * ks) : u32x4{0, 0, 0, 0};
+  if (k0 < k1) issue(k0, 0);
+  for (int kk = k0, st = 0; kk < k1; kk += KSTEP, st ^= 1) {
+    if (kk + KSTEP < k1) {
+      // the other stage was last read by the previous step: its reads are done
+      // before the next copy into it is issued
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(kk + KSTEP, st ^ 1);
+      wait_vmcnt<LOADS>();
+    } else {
+      wait_vmcnt0();
     }
-    u32x4 vr[VLOADS];
-#pragma unroll
-    for (int j = 0; j < VLOADS; ++j) {
-      const int cid = lane + 64 * j;
-      const int r = cid / NCH, ch = cid % NCH;
-      const int key = kk + r;
-      vr[j] = key < k1 ? ldg16_stream(vb0 + (size_t)key * row + 8 * ch) : u32x4{0, 0, 0, 0};
-    }
+    const char* ks_lds = lds + st * LD::STAGE;
+    const bf16* vs = reinterpret_cast<const bf16*>(ks_lds + LD::KBYTES);
     // ---- S^T = K Q^T: lane -> query n, keys kk + 16*h + 4*grp + i
     f32x4 s0 = f32x4{}, s1 = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s0 = mfma16(__builtin_bit_cast(bf16x8, ka[0][ks]), qr[ks], s0);
-      s1 = mfma16(__builtin_bit_cast(bf16x8, ka[1][ks]), qr[ks], s1);
+      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(ks_lds + krd[ks]);
+      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(ks_lds + krd[ks] + 16 * DK * 2);
+      s0 = mfma16(ka0, qr[ks], s0);
+      s1 = mfma16(ka1, qr[ks], s1);
     }
     if (kk + KSTEP > k1) {
 #pragma unroll
@@ -155,14 +228,7 @@ __device__ __forceinline__ void attend_range(const Args& a, bf16* vs, int b, int
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
 
-    // ---- V rows to LDS, then O^T += V^T P^T
-#pragma unroll
-    for (int j = 0; j < VLOADS; ++j) {
-      const int cid = lane + 64 * j;
-      const int r = cid / NCH, ch = cid % NCH;
-      sts16(&vs[v_phys<D>(r, 8 * ch)], vr[j]);
-    }
-    __syncthreads();
+    // ---- O^T += V^T P^T, V^T read from LDS with the transposing read
     {
       const int r0 = 4 * grp + (n >> 2);
 #pragma unroll
@@ -173,7 +239,6 @@ __device__ __forceinline__ void attend_range(const Args& a, bf16* vs, int b, int
         o[db] = mfma16(concat(va, vb), pb, o[db]);
       }
     }
-    __syncthreads();
   }
 
   // ---- partial state per query head: acc[d] (unnormalised), m, l
@@ -194,7 +259,7 @@ __device__ __forceinline__ void attend_range(const Args& a, bf16* vs, int b, int
 // pieces of the same cache rows.
 template <int D, int DK>
 __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) bf16 vs[KSTEP * D];
+  __shared__ __attribute__((aligned(16))) char lds[DecodeLds<D, DK>::BYTES];
   const int g = blockIdx.x % a.Hkv;
   const int s = (blockIdx.x / a.Hkv) % a.S;
   const int b = blockIdx.x / (a.Hkv * a.S);
@@ -206,7 +271,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Args a) {
   const int k0 = max(s * a.chunk, lo);
   const int k1 = min(Lb, s * a.chunk + a.chunk);
   const int rec = D + 4;
-  attend_range<D, DK>(a, vs, b, g, k0, k1, a.ws + ((size_t)(b * a.Hq + g * a.nq) * a.S + s) * rec,
+  attend_range<D, DK>(a, lds, b, g, k0, k1, a.ws + ((size_t)(b * a.Hq + g * a.nq) * a.S + s) * rec,
                       (size_t)a.S * rec);
 }
 
@@ -249,7 +314,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int* seq_lens, 
 // in slot w + b (unique: a later range never reaches back to an earlier sequence).
 template <int D, int DK>
 __global__ __launch_bounds__(64) void decode_flat_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) bf16 vs[KSTEP * D];
+  __shared__ __attribute__((aligned(16))) char lds[DecodeLds<D, DK>::BYTES];
   const int g = blockIdx.x % a.Hkv;
   const int w = blockIdx.x / a.Hkv;
   const int* plan = a.plan;
@@ -272,7 +337,7 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(Args a) {
       const int Lb = min(a.L, max(1, a.seq_lens[b]));
       const int lo = a.window > 0 ? max(0, Lb - a.window) : 0;
       const int k0 = lo + (x - plan[b]);
-      attend_range<D, DK>(a, vs, b, g, k0, k0 + (seg_end - x),
+      attend_range<D, DK>(a, lds, b, g, k0, k0 + (seg_end - x),
                           a.ws + ((size_t)(g * a.nq) * a.nslot + w + b) * rec, hstride);
       x = seg_end;
     }
