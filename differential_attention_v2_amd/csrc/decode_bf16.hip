@@ -345,39 +345,71 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(Args a) {
   }
 }
 
-// Merge the S partial states of one query head (records at base): lane owns
-// D/64 consecutive columns of the normalised output.  All records are requested
-// before any is used, so a merge costs about one memory round trip.
-template <int D>
-__device__ __forceinline__ void merge_head(const float* base, int S, int lane, float (&o)[D / 64]) {
+// Merge the S partial states of NH query heads (records at base[h]): lane owns
+// D/64 consecutive columns of each normalised output.  Records are requested UNR
+// key ranges at a time for all NH heads before any is used, with a running
+// maximum raised per batch, so up to UNR ranges cost one memory round trip (and
+// the result equals a merge against the true maximum computed first).
+template <int D, int NH, int UNR>
+__device__ __forceinline__ void merge_heads_n(const float* const (&base)[NH], int S, int lane, float (&o)[NH][D / 64]) {
   constexpr int E = D / 64;
-  constexpr int UNR = 8;               // key ranges in flight per batch of loads
   const int rec = D + 4;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, base[s * rec + D]);
-  float acc[E], den = 0.f;
+  float M[NH], den[NH], acc[NH][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int h = 0; h < NH; ++h) {
+    M[h] = -INFINITY;
+    den[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+  }
   for (int s0 = 0; s0 < S; s0 += UNR) {
-    float ms[UNR], ls[UNR], av[UNR][E];
+    float ms[NH][UNR], ls[NH][UNR], av[NH][UNR][E];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int s = min(s0 + u, S - 1);
-      ms[u] = base[s * rec + D];
-      ls[u] = base[s * rec + D + 1];
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int e = 0; e < E; ++e) av[u][e] = base[s * rec + E * lane + e];
-    }
+      for (int u = 0; u < UNR; ++u) {
+        const float* r = base[h] + min(s0 + u, S - 1) * rec;
+        ms[h][u] = r[D];
+        ls[h][u] = r[D + 1];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const float wgt = (s0 + u >= S || ms[u] == -INFINITY) ? 0.f : fast_exp2(ms[u] - M);
-      den += wgt * ls[u];
+        for (int e = 0; e < E; ++e) av[h][u][e] = r[E * lane + e];
+      }
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += wgt * av[u][e];
+    for (int h = 0; h < NH; ++h) {
+      float mb = M[h];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        if (s0 + u < S) mb = fmaxf(mb, ms[h][u]);
+      if (mb != M[h]) {   // rescale what earlier batches gathered (nothing, for the first)
+        const float r = M[h] == -INFINITY ? 0.f : fast_exp2(M[h] - mb);
+        den[h] *= r;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] *= r;
+        M[h] = mb;
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const float wgt = (s0 + u >= S || ms[h][u] == -INFINITY) ? 0.f : fast_exp2(ms[h][u] - M[h]);
+        den[h] += wgt * ls[h][u];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] += wgt * av[h][u][e];
+      }
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = acc[e] / den;
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[h][e] = acc[h][e] / den[h];
+}
+
+// batches of 4 key ranges for short merges (the split decode of a long batch
+// has 2), 16 otherwise
+template <int D, int NH>
+__device__ __forceinline__ void merge_heads(const float* const (&base)[NH], int S, int lane, float (&o)[NH][D / 64]) {
+  if (S <= 4)
+    merge_heads_n<D, NH, 4>(base, S, lane, o);
+  else
+    merge_heads_n<D, NH, 16>(base, S, lane, o);
 }
 
 // One wave per (b, pair): o_1 - lambda o_2 (optional V1 RMSNorm), bf16 out.
@@ -389,8 +421,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(Args a) {
   const int lane = threadIdx.x;
   const int rec = D + 4;
   float o[2][E];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) merge_head<D>(a.ws + ((size_t)b * a.Hq + 2 * p + h) * a.S * rec, a.S, lane, o[h]);
+  const float* const base[2] = {a.ws + ((size_t)b * a.Hq + 2 * p) * a.S * rec, a.ws + ((size_t)b * a.Hq + 2 * p + 1) * a.S * rec};
+  merge_heads<D, 2>(base, a.S, lane, o);
   const float lamv = a.lam[(size_t)b * a.P + p];
   float x[E], ss = 0.f;
 #pragma unroll
@@ -418,17 +450,20 @@ __global__ __launch_bounds__(64) void compare_combine_kernel(Args a, const float
   const int bh = blockIdx.x;
   const int lane = threadIdx.x;
   const int rec = D + 4;
-  float o1[E], o2[E];
-  merge_head<D>(a.ws + (size_t)bh * a.S * rec, a.S, lane, o1);
   float x[E], ss = 0.f;
   if (ws2 != nullptr) {
-    merge_head<D>(ws2 + (size_t)bh * a.S * rec, a.S, lane, o2);
+    float o[2][E];
+    const float* const base[2] = {a.ws + (size_t)bh * a.S * rec, ws2 + (size_t)bh * a.S * rec};
+    merge_heads<D, 2>(base, a.S, lane, o);
     const float lamv = a.lam[bh];
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = o1[e] - lamv * o2[e];
+    for (int e = 0; e < E; ++e) x[e] = o[0][e] - lamv * o[1][e];
   } else {
+    float o[1][E];
+    const float* const base[1] = {a.ws + (size_t)bh * a.S * rec};
+    merge_heads<D, 1>(base, a.S, lane, o);
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = o1[e];
+    for (int e = 0; e < E; ++e) x[e] = o[0][e];
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) ss += x[e] * x[e];
@@ -455,9 +490,9 @@ __global__ __launch_bounds__(64) void decode_flat_combine_kernel(Args a) {
   const int Kw = a.plan[a.B + 1];
   const int w0 = a.plan[b] / Kw, w1 = (a.plan[b + 1] - 1) / Kw;
   float o[2][E];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    merge_head<D>(a.ws + ((size_t)(2 * p + h) * a.nslot + w0 + b) * rec, w1 - w0 + 1, lane, o[h]);
+  const float* const base[2] = {a.ws + ((size_t)(2 * p) * a.nslot + w0 + b) * rec,
+                                a.ws + ((size_t)(2 * p + 1) * a.nslot + w0 + b) * rec};
+  merge_heads<D, 2>(base, w1 - w0 + 1, lane, o);
   const float lamv = a.lam[(size_t)b * a.P + p];
   float x[E], ss = 0.f;
 #pragma unroll
