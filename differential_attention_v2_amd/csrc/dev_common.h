@@ -29,8 +29,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
-
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -56,8 +54,6 @@ __device__ __forceinline__ float partner32(float v, bool lo) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
-
 // Sum of the two bf16 values of a packed pair, accumulated in fp32.
 __device__ __forceinline__ float dot2_ones(bf16x2 p, float acc) {
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
@@ -65,25 +61,15 @@ __device__ __forceinline__ float dot2_ones(bf16x2 p, float acc) {
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-// Streaming 16-byte load (nontemporal hint): data read exactly once, as the
-// decode KV cache is, need not displace reusable lines.
-__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16*l (lds_base wave-uniform).  Issued as inline asm so the compiler
-// does not insert conservative vmcnt waits in front of unrelated LDS reads; the
-// caller waits with wait_vmcnt0() before the barrier that publishes the data.
-__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
-  const uint32_t lds = (uint32_t)(uintptr_t)LDS_PTR(const char, lds_base);
-  // one wait state between the M0 write and the LDS-DMA load that reads it
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr) : "memory", "m0");
-}
-// Same copy with a scalar 64-bit base and a per-lane 32-bit byte offset (the
-// "saddr" form): no per-lane 64-bit address arithmetic.  lds_addr is the
-// wave-uniform LDS byte address of lane 0's 16 bytes.
+// Direct global -> LDS copy of 16 bytes per lane with a scalar 64-bit base and a
+// per-lane 32-bit byte offset (the "saddr" form: no per-lane 64-bit address
+// arithmetic): lane l's bytes land at lds_addr + 16*l, lds_addr being the
+// wave-uniform LDS byte address of lane 0's 16 bytes.  Issued as inline asm so the
+// compiler does not insert conservative vmcnt waits in front of unrelated LDS
+// reads; the caller waits on vmcnt before the barrier that publishes the data.
 __device__ __forceinline__ void dma16_saddr(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  // one wait state between the M0 write and the copy that reads it
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
@@ -94,6 +80,5 @@ __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)
 // vmcnt(0) as a builtin (expcnt/lgkmcnt left at their maxima), visible to the
 // compiler's own wait-count tracking: loads issued before it need no later wait.
 __device__ __forceinline__ void wait_vmcnt0_builtin() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-__device__ __forceinline__ void sts16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace diffattn

@@ -74,12 +74,8 @@ struct Args {
 };
 
 // LDS layouts: tiles are row-major [key][d] without padding; 16-byte chunks of a
-// row are XOR-permuted so that the MFMA operand reads hit distinct banks.
-template <int D>
-__device__ __forceinline__ int k_phys(int row, int col) {   // col in elements
-  constexpr int NCH = D / 8;
-  return row * D + ((((col >> 3) ^ (row & (NCH - 1)))) << 3) + (col & 7);
-}
+// row are XOR-permuted so that the MFMA operand reads hit distinct banks (K: chunk
+// ^ (row % chunks per row); V: chunk ^ v_swz(row)).
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
   return (D >= 128) ? ((row & 3) << 2) : ((row & 1) << 2);
