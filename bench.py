@@ -61,7 +61,7 @@ def cpu_baseline(budget_s: float) -> dict:
         threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas")
     except Exception:  # noqa: BLE001
         threads = os.cpu_count()
-    w = W.CONFIGS[2]
+    w = W.PREFILL_T4096
     inp = W.make_prefill(w)
     q, k, v = (W.to_f64(inp[n], "bf16") for n in ("q", "k", "v"))
     G = w.G
@@ -76,7 +76,7 @@ def cpu_baseline(budget_s: float) -> dict:
     dt = time.perf_counter() - t0
     flops = w.prefill_flops() * done / w.P
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads or 1), "kind": "oracle",
-            "sample": f"c2 prefill, {done} pair passes ({w.P} pairs in the workload) x all {w.T} rows, "
+            "sample": f"T={w.T} prefill, {done} pair passes ({w.P} pairs in the workload) x all {w.T} rows, "
                       f"fp64 numpy (OpenBLAS), {dt:.1f} s"}
 
 
@@ -114,7 +114,7 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU sharding or collectives)", file=sys.stderr)
         return 2
 
@@ -131,7 +131,7 @@ def main() -> int:
     def dev_bf16(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    wp, wd = W.CONFIGS[2], W.CONFIGS[4]
+    wp, wd = W.PREFILL_T4096, W.DECODE_B64_L8192
     do_p = args.only in (None, "prefill")
     do_d = args.only in (None, "decode")
     do_b = args.only == "backward" or (args.only is None and not args.no_backward)
@@ -195,7 +195,7 @@ def main() -> int:
     bwd = None
     if do_b:
         # training step of the attention core: training forward (out, o2, lse) and
-        # backward, timed after the main step, on the same c2 inputs
+        # backward, timed after the main step, on the same T=4096 prefill inputs
         if not do_p:
             ip = W.make_prefill(wp)
             pq, pk, pv = dev_bf16(ip["q"]), dev_bf16(ip["k"]), dev_bf16(ip["v"])
@@ -236,8 +236,8 @@ def main() -> int:
 
     serving = None
     if do_s:
-        # serving variants on the same shapes: the c2 prefill with a 1024-key causal
-        # window, and the c4 decode over caches with lengths uniform in [1, 8192]
+        # serving variants on the same shapes: the T=4096 prefill with a 1024-key causal
+        # window, and the B=64, L=8192 decode over caches with lengths uniform in [1, 8192]
         SWA = 1024
         if not (do_p or do_b):
             ip = W.make_prefill(wp)
@@ -291,7 +291,7 @@ def main() -> int:
 
     layouts = None
     if do_l:
-        # decode-speed claim of the pages: on the c4 cache geometry (B=64, L=8192,
+        # decode-speed claim of the pages: on the B=64, L=8192 cache geometry (
         # Hkv=8, d=128) time a standard transformer with H=32 heads, DIFF V1 with
         # the same 32 heads (q, k halves per branch, V read once per branch) and V2
         # (64 query heads = 32 pairs, the bench's decode)
@@ -337,7 +337,7 @@ def main() -> int:
 
     projections = None
     if do_j:
-        # the steps either side of the c2 attention core: lambda for 4096 tokens x 32
+        # the steps either side of the T=4096 attention core: lambda for 4096 tokens x 32
         # pairs from d_model = 4096, and O_W from P*d = 4096 back to d_model = 4096
         rows, dm, kin = wp.B * wp.T, wp.P * wp.d, wp.P * wp.d
         ij = W.make_projections(rows, dm, wp.P, kin, dm)
@@ -381,7 +381,7 @@ def main() -> int:
         # Inputs are drawn on the device from a seeded generator with the same
         # distributions as the host generator (host generation of 4.3 GB of cache
         # would take minutes).
-        w3, w5 = W.CONFIGS[3], W.CONFIGS[5]
+        w3, w5 = W.PREFILL_T32768, W.DECODE_B8_L131072
         gen = torch.Generator(device=dev)
         gen.manual_seed(3000 + 3)
 

@@ -145,18 +145,17 @@ class Workload:
 
 
 # The five workloads the hot path is measured and checked on.
-CONFIGS: dict[int, Workload] = {
-    1: Workload("c1_tiny_prefill_fp32", "prefill", "fp32", B=1, T=128, Hq=2, Hkv=1, d=64,
-                qkv_scale=1.0, seed=1001),
-    2: Workload("c2_prefill_T4096", "prefill", "bf16", B=1, T=4096, Hq=64, Hkv=8, d=128,
-                qkv_scale=1.0 / math.sqrt(2.0), seed=1002),
-    3: Workload("c3_prefill_T32768", "prefill", "bf16", B=1, T=32768, Hq=64, Hkv=8, d=128,
-                qkv_scale=1.0 / math.sqrt(2.0), seed=1003),
-    4: Workload("c4_decode_B64_L8192", "decode", "bf16", B=64, T=8192, Hq=64, Hkv=8, d=128,
-                qkv_scale=1.0, seed=1004),
-    5: Workload("c5_decode_B8_L131072", "decode", "bf16", B=8, T=131072, Hq=64, Hkv=8, d=128,
-                qkv_scale=1.0, seed=1005),
-}
+TINY_PREFILL_FP32 = Workload("prefill_fp32_T128", "prefill", "fp32", B=1, T=128, Hq=2, Hkv=1, d=64,
+                             qkv_scale=1.0, seed=1001)
+PREFILL_T4096 = Workload("prefill_T4096", "prefill", "bf16", B=1, T=4096, Hq=64, Hkv=8, d=128,
+                         qkv_scale=1.0 / math.sqrt(2.0), seed=1002)
+PREFILL_T32768 = Workload("prefill_T32768", "prefill", "bf16", B=1, T=32768, Hq=64, Hkv=8, d=128,
+                          qkv_scale=1.0 / math.sqrt(2.0), seed=1003)
+DECODE_B64_L8192 = Workload("decode_B64_L8192", "decode", "bf16", B=64, T=8192, Hq=64, Hkv=8, d=128,
+                            qkv_scale=1.0, seed=1004)
+DECODE_B8_L131072 = Workload("decode_B8_L131072", "decode", "bf16", B=8, T=131072, Hq=64, Hkv=8, d=128,
+                             qkv_scale=1.0, seed=1005)
+WORKLOADS = (TINY_PREFILL_FP32, PREFILL_T4096, PREFILL_T32768, DECODE_B64_L8192, DECODE_B8_L131072)
 
 
 def _streams(seed: int) -> list[np.random.SeedSequence]:

@@ -98,9 +98,9 @@ def test_backward_small(gpu_device, shape):
     _check_grads(_case(B, T, Hq, Hkv, d, causal, seed=7000 + T), gpu_device)
 
 
-def test_backward_c2_shape_sampled_groups(gpu_device):
+def test_backward_T4096_sampled_groups(gpu_device):
     """The bench shape (B=1, T=4096, Hq=64, Hkv=8, d=128, causal), two KV groups checked in full."""
-    w = W.CONFIGS[2]
+    w = W.PREFILL_T4096
     _check_grads(w, gpu_device, groups=[0, 5])
 
 

@@ -45,11 +45,11 @@ def test_v1_layout_decode(gpu_device, shape):
     assert np.isfinite(got).all() and rel <= 1e-2
 
 
-def test_compare_c4_cache_shape(gpu_device):
+def test_compare_B64_L8192_cache_shape(gpu_device):
     """B=64, L=8192, Hkv=8, d=128 caches with H=32 heads (the V2 workload's 32 pairs), 4 sequences checked."""
     inp, (q, k, v, lam), f = _inputs(64, 8192, 32, 8, 128, 9200, gpu_device)
     sel = np.array([0, 21, 42, 63])
     got = from_device(bd.decode_standard(q, k, v))[sel]
-    assert_parity(got, oracle.standard_decode(*f, batches=sel), "standard c4 cache")
+    assert_parity(got, oracle.standard_decode(*f, batches=sel), "standard, B=64 L=8192 cache")
     got = from_device(bd.decode_v1_layout(q, k, v, lam, v1_rmsnorm=False))[sel]
-    assert_parity(got, oracle.v1_layout_decode(*f, inp["lam"], v1_rmsnorm=False, batches=sel), "V1 layout c4 cache")
+    assert_parity(got, oracle.v1_layout_decode(*f, inp["lam"], v1_rmsnorm=False, batches=sel), "V1 layout, B=64 L=8192 cache")

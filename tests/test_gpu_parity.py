@@ -45,42 +45,42 @@ def _decode_case(w: W.Workload, dev, batches=None, pairs=None, splits=0, v1=Fals
 
 
 # ------------------------------------------------------------------ the five workloads
-def test_c1_tiny_fp32(gpu_device):
-    got, ref = _prefill_case(W.CONFIGS[1], gpu_device)
-    err = assert_parity(got, ref, "c1 fp32 T=128")
+def test_tiny_prefill_fp32(gpu_device):
+    got, ref = _prefill_case(W.TINY_PREFILL_FP32, gpu_device)
+    err = assert_parity(got, ref, "fp32 prefill T=128")
     assert err["max_abs"] < 1e-4     # fp32 all the way
 
 
-def test_c2_prefill_full(gpu_device):
-    got, ref = _prefill_case(W.CONFIGS[2], gpu_device)
-    assert_parity(got, ref, "c2 bf16 T=4096 all rows")
+def test_prefill_T4096_all_rows(gpu_device):
+    got, ref = _prefill_case(W.PREFILL_T4096, gpu_device)
+    assert_parity(got, ref, "bf16 prefill T=4096 all rows")
 
 
-def _c3_rows(T, seed=3):
+def _sampled_rows(T, seed=3):
     rng = np.random.default_rng(seed)
     edges = np.concatenate([[t - 1, t] for t in range(64, T, 4096)])
     rows = np.concatenate([np.arange(128), np.arange(T - 128, T), edges, rng.choice(T, 256, replace=False)])
     return np.unique(rows[(rows >= 0) & (rows < T)])
 
 
-def test_c3_prefill_sampled_rows(gpu_device):
-    w = W.CONFIGS[3]
-    rows = _c3_rows(w.T)
+def test_prefill_T32768_sampled_rows(gpu_device):
+    w = W.PREFILL_T32768
+    rows = _sampled_rows(w.T)
     got, ref = _prefill_case(w, gpu_device, rows=rows)
-    assert_parity(got, ref, f"c3 bf16 T=32768 ({rows.size} sampled rows, all pairs)")
+    assert_parity(got, ref, f"bf16 prefill T=32768 ({rows.size} sampled rows, all pairs)")
 
 
-def test_c4_decode(gpu_device):
-    w = W.CONFIGS[4]
+def test_decode_B64_L8192(gpu_device):
+    w = W.DECODE_B64_L8192
     got, ref = _decode_case(w, gpu_device, batches=[0, 1, 13, 31, 32, 47, 62, 63])
-    assert_parity(got, ref, "c4 decode B=64 L=8192 (8 batches, all pairs)")
+    assert_parity(got, ref, "decode B=64 L=8192 (8 batches, all pairs)")
 
 
-def test_c5_decode_and_v1_mode(gpu_device):
-    w = W.CONFIGS[5]
+def test_decode_B8_L131072_and_v1_mode(gpu_device):
+    w = W.DECODE_B8_L131072
     b, p = [0, 5], [0, 9, 18, 31]
     got, ref = _decode_case(w, gpu_device, batches=b, pairs=p)
-    assert_parity(got, ref, "c5 decode B=8 L=131072")
+    assert_parity(got, ref, "decode B=8 L=131072")
     vec = W.make_v1_lambda_vectors(w.P)
     lam1 = oracle.v1_lambda(vec["lq1"], vec["lk1"], vec["lq2"], vec["lk2"], 0.8)
     # the V1 lambda through the library's own kernel, checked against the oracle
@@ -89,7 +89,7 @@ def test_c5_decode_and_v1_mode(gpu_device):
     np.testing.assert_allclose(lam_dev.cpu().numpy(), np.broadcast_to(lam1, (w.B, w.P)), rtol=2e-6, atol=2e-6)
     got, ref = _decode_case(w, gpu_device, batches=b, pairs=p, v1=True, eps=1e-5,
                             lam=lam_dev.cpu().numpy())
-    assert_parity(got, ref, "c5 decode V1 mode (exp-dot lambda, RMSNorm eps=1e-5)")
+    assert_parity(got, ref, "decode B=8 L=131072 V1 mode (exp-dot lambda, RMSNorm eps=1e-5)")
 
 
 # ------------------------------------------------------------------ edge shapes
@@ -187,7 +187,7 @@ def test_identical_branches_cancel_exactly(gpu_device):
 
 def test_deterministic(gpu_device):
     dev = gpu_device
-    w = W.CONFIGS[2].with_(T=1024)
+    w = W.PREFILL_T4096.with_(T=1024)
     inp = W.make_prefill(w)
     q, k, v = (to_device(inp[n], "bf16", dev) for n in ("q", "k", "v"))
     lam = torch.from_numpy(inp["lam"]).to(dev)
@@ -206,7 +206,7 @@ def test_v1_mode_prefill(gpu_device):
     output x: y_gpu * sqrt(mean(x_ref^2) + eps) against x_ref.  The normalised
     output itself must match to rel-L2 <= 1e-2.
     """
-    w = W.CONFIGS[2].with_(T=512, seed=44)
+    w = W.PREFILL_T4096.with_(T=512, seed=44)
     eps = 1e-5
     inp = W.make_prefill(w)
     dev = gpu_device
@@ -221,8 +221,8 @@ def test_v1_mode_prefill(gpu_device):
     assert err["rel_l2"] <= 1e-2
 
 
-def test_noncausal_matches_oracle_c2_shape(gpu_device):
-    w = W.CONFIGS[2].with_(T=640, causal=False, seed=45)
+def test_noncausal_matches_oracle_T4096_shape(gpu_device):
+    w = W.PREFILL_T4096.with_(T=640, causal=False, seed=45)
     got, ref = _prefill_case(w, gpu_device)
     assert_parity(got, ref, "non-causal prefill T=640")
 

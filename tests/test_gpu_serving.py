@@ -61,16 +61,16 @@ def test_prefill_window_v1_mode(gpu_device):
     assert rel <= 1e-2
 
 
-def test_prefill_window_c2_shape_sampled_rows(gpu_device):
+def test_prefill_window_T4096_sampled_rows(gpu_device):
     """B=1, T=4096, Hq=64, Hkv=8, d=128 with the lesson's 1024-key window, 200 rows checked."""
-    w = W.CONFIGS[2]
+    w = W.PREFILL_T4096
     inp, (q, k, v, lam) = _prefill_inputs(w, gpu_device)
     out = from_device(bd.prefill_window(q, k, v, lam, 1024))
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([np.arange(0, 8), [1023, 1024, 1025, 4095], rng.choice(4096, 188, False)]))
     ref = oracle.diffattn_prefill(*(W.to_f64(inp[n], "bf16") for n in ("q", "k", "v")), inp["lam"], causal=True,
                                   window=1024, rows=rows)
-    assert_parity(out[:, rows], ref, "c2 window=1024 sampled rows")
+    assert_parity(out[:, rows], ref, "prefill T=4096 window=1024 sampled rows")
 
 
 # --------------------------------------------------------------------------------- decode
@@ -136,9 +136,9 @@ def test_decode_varlen_clamps_out_of_range_lengths(gpu_device):
     assert_parity(got, ref, "clamped lengths")
 
 
-def test_decode_varlen_c4_shape_sampled(gpu_device):
+def test_decode_varlen_B64_L8192_sampled(gpu_device):
     """B=64, L=8192, Hq=64, Hkv=8, d=128 with lengths uniform in [1, 8192]; 8 sequences checked."""
-    w = W.CONFIGS[4]
+    w = W.DECODE_B64_L8192
     inp, (q, k, v, lam) = _decode_inputs(w, gpu_device)
     lens_np = W.ragged_lengths(w.B, w.T)
     lens = torch.from_numpy(lens_np).to(gpu_device)
@@ -146,4 +146,4 @@ def test_decode_varlen_c4_shape_sampled(gpu_device):
     bsel = np.array([0, 1, 13, 31, 32, 47, 62, 63])
     ref = oracle.diffattn_decode(*(W.to_f64(inp[n], "bf16") for n in ("q", "k", "v")), inp["lam"], batches=bsel,
                                  seq_lens=lens_np)
-    assert_parity(got[bsel], ref, "c4 ragged lengths (8 sequences)")
+    assert_parity(got[bsel], ref, "decode B=64 L=8192 ragged lengths (8 sequences)")

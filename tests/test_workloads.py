@@ -16,7 +16,7 @@ def test_bf16_rounding_matches_torch_rne():
 
 
 def test_generation_is_deterministic_and_chunk_stable(monkeypatch):
-    w = W.CONFIGS[1]
+    w = W.TINY_PREFILL_FP32
     a = W.make_prefill(w)
     b = W.make_prefill(w)
     for key in ("q", "k", "v", "lam"):
@@ -33,13 +33,13 @@ def test_generation_is_deterministic_and_chunk_stable(monkeypatch):
 
 
 def test_distribution_scale():
-    w = W.CONFIGS[2].with_(T=512)
+    w = W.PREFILL_T4096.with_(T=512)
     x = W.bf16_to_f32(W.make_prefill(w)["q"])
     assert abs(x.std() - 1 / np.sqrt(2)) < 0.01 and abs(x.mean()) < 0.01
 
 
 def test_signal_planting():
-    w = W.CONFIGS[3].with_(T=2048, Hkv=2, Hq=16)
+    w = W.PREFILL_T32768.with_(T=2048, Hkv=2, Hq=16)
     inp = W.plant_signal(w, W.make_prefill(w))
     plan = inp["plan"]
     assert len(plan) == w.B * w.Hkv * w.G * 8
