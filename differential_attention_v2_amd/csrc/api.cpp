@@ -15,10 +15,12 @@ namespace {
 constexpr int kVersion = 100;                    // 0.1.0
 constexpr long long kMaxElems = 1LL << 40;       // per tensor
 constexpr long long kMaxGrid = (1LL << 31) - 1;  // workgroups per launch
-// Decode split target: one wave per SIMD of MI355X (256 CUs x 4).  Measured on
-// the device, fewer and longer cache streams read faster than more and shorter
-// ones (B=64 L=8192: 6.0 TB/s with 1024 waves, 5.5 TB/s with 4096).
-constexpr int kDecodeTargetWaves = 1024;
+// Decode split target: two waves per CU of MI355X (256 CUs).  Each wave keeps its
+// next step's cache rows in flight through two LDS stages, and fewer, longer cache
+// streams read faster than more, shorter ones: on the device B=64 L=8192 reads
+// 6.6 TB/s with 512 waves, 6.5 with 1024 (5.5 with 4096 before the LDS staging);
+// ragged caches of the same shape take 183 us with 512 waves and 188 with 1024.
+constexpr int kDecodeTargetWaves = 512;
 
 bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -185,7 +187,7 @@ int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
 }
 
 namespace {
-// ranges per KV head of the even split over ragged caches: about one wave per SIMD
+// ranges per KV head of the even split over ragged caches: the same wave target
 int varlen_ranges(int Hkv, int num_splits) {
   return num_splits > 0 ? num_splits : (kDecodeTargetWaves + Hkv - 1) / Hkv;
 }

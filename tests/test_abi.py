@@ -109,16 +109,17 @@ def test_v1_lambda_rejects(lib):
 
 
 def test_decode_split_plan(lib):
-    # B*Hkv (b, KV head) units are split so that ~1024 waves (one per SIMD) stream the cache
-    assert bd.diffattn_decode_num_splits(64, 8192, 64, 8, 128) == 2
-    assert bd.diffattn_decode_num_splits(8, 131072, 64, 8, 128) == 16
+    # B*Hkv (b, KV head) units are split so that ~512 waves (two per CU) stream the cache
+    assert bd.diffattn_decode_num_splits(64, 8192, 64, 8, 128) == 1
+    assert bd.diffattn_decode_num_splits(8, 131072, 64, 8, 128) == 8
+    assert bd.diffattn_decode_num_splits(16, 8192, 64, 8, 128) == 4
     assert bd.diffattn_decode_num_splits(512, 1000, 64, 8, 128) == 1
     assert bd.diffattn_decode_num_splits(1, 1, 2, 1, 64) == 1
     assert bd.diffattn_decode_num_splits(1, 100, 2, 1, 64) == 4       # ceil(100/32) ranges of 32
     assert bd.diffattn_decode_num_splits(1, 100, 3, 1, 64) == 0       # invalid heads
     rec = 128 + 4
-    assert bd.diffattn_decode_workspace_bytes(64, 8192, 64, 8, 128, 0) == 64 * 64 * 2 * rec * 4
-    assert bd.diffattn_decode_workspace_bytes(8, 131072, 64, 8, 128, 0) == 8 * 64 * 16 * rec * 4
+    assert bd.diffattn_decode_workspace_bytes(64, 8192, 64, 8, 128, 0) == 64 * 64 * 1 * rec * 4
+    assert bd.diffattn_decode_workspace_bytes(8, 131072, 64, 8, 128, 0) == 8 * 64 * 8 * rec * 4
     assert bd.diffattn_decode_workspace_bytes(64, 8192, 64, 8, 128, 8) == 64 * 64 * 8 * rec * 4
     # explicit split counts are clamped to the number of 32-key blocks and never leave a range empty
     assert bd.diffattn_decode_workspace_bytes(1, 100, 2, 1, 64, 1000) == 1 * 2 * 4 * (64 + 4) * 4
@@ -243,7 +244,7 @@ def test_output_proj_rejects(lib):
 
 def test_varlen_workspace_bytes(lib):
     # max of the per-(b, KV head) split records and the even-split records + plan
-    split = 64 * 64 * 2 * 132 * 4
-    flat = 64 * (128 + 64) * 132 * 4 + (64 + 2) * 4
+    split = 64 * 64 * 1 * 132 * 4                   # S = 1 key range per (b, KV head)
+    flat = 64 * (64 + 64) * 132 * 4 + (64 + 2) * 4  # 512 / 8 = 64 ranges per KV head
     assert bd.diffattn_decode_varlen_workspace_bytes(64, 8192, 64, 8, 128, 0) == max(split, flat)
     assert bd.diffattn_decode_varlen_workspace_bytes(64, 8192, 62, 8, 128, 0) == 0
