@@ -607,6 +607,9 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
         o[1] = *reinterpret_cast<const bf16x8*>(lds + VO + ro + aofs[s]);
       };
       load_kv(0, kva[0]);
+      // raised issue priority while these products issue, as in the forward: the
+      // other wave of the SIMD then tends to run its dS and dQ work meanwhile
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         if (s + 1 < KSTEPS) load_kv(s + 1, kva[(s + 1) & 1]);
@@ -614,6 +617,7 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
         st = mfma32(kva[s & 1][0], qreg[s], st);
         dpt = mfma32(kva[s & 1][1], oreg[s], dpt);
       }
+      __builtin_amdgcn_s_setprio(0);
       // hidden keys (future, or past T) get score -inf: P and dS come out 0
       if ((a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T) {
 #pragma unroll
