@@ -458,7 +458,9 @@ def main() -> int:
                          "splits": bd.diffattn_decode_num_splits(wd.B, wd.T, wd.Hq, wd.Hkv, wd.d)}
         res["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": gbs / PEAK_HBM_GBS, "traffic": _traffic("decode"),
-                                  "kernel": "decode_split_kernel<128, 128> + decode_combine_kernel<128>",
+                                  "kernel": ("decode_split_kernel<128, 128>" if bd.diffattn_decode_num_splits(
+                                      wd.B, wd.T, wd.Hq, wd.Hkv, wd.d) == 1 else
+                                             "decode_split_kernel<128, 128> + decode_combine_kernel<128>"),
                                   "algorithmic_bytes_per_launch": wd.decode_kv_bytes()}
         if not do_p:
             res.update(value=gbs, unit="GB/s")

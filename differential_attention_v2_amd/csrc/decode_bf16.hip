@@ -57,6 +57,7 @@ struct Args {
   int qoff, koff;        // start of the dot-product slice within q and k rows
   const int* plan;       // ragged caches: row offsets per sequence, total, rows per range
   int nslot;             // ragged caches: record slots per query head
+  int fuse;              // one key range per sequence: the split kernel writes out itself
 };
 
 // V rows in LDS: row-major [key][d], 16-byte chunks XOR-permuted per row so the
@@ -241,9 +242,44 @@ __device__ __forceinline__ void attend_range(const Args& a, char* lds, int b, in
     }
   }
 
-  // ---- partial state per query head: acc[d] (unnormalised), m, l
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  if (a.fuse) {
+    // The wave has seen every key of the sequence: each head's output is acc / l,
+    // and the pair's two heads (head n of the group is branch n & 1 of pair
+    // (g nq + n) / 2) sit in lanes n and n^1 with the same d, so o_1 - lambda o_2
+    // (optional V1 RMSNorm) is finished here and no records are written.
+    const bool head0 = (n & 1) == 0 && n < nq;
+    const int p = (g * nq + n) >> 1;
+    const float lamv = head0 ? a.lam[(size_t)b * a.P + p] : 0.f;
+    float x[DB][4], ss = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = o[db][i] / l;
+        const float y2 = __shfl_xor(y, 1);
+        x[db][i] = y - lamv * y2;
+        ss += x[db][i] * x[db][i];
+      }
+    if (a.v1) {   // lanes n, n^16, n^32, n^48 hold the pair's D values
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[db][i] *= r;
+    }
+    if (head0) {
+      bf16* dst = a.out + ((size_t)b * a.P + p) * D + 4 * grp;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<bf16x4*>(dst + 16 * db) = bf16x4{(bf16)x[db][0], (bf16)x[db][1], (bf16)x[db][2], (bf16)x[db][3]};
+    }
+    return;
+  }
+  // ---- partial state per query head: acc[d] (unnormalised), m, l
   if (n >= nq) return;
   float* w = rec0 + n * hstride;
 #pragma unroll
@@ -537,6 +573,7 @@ hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
   a.qoff = a.koff = 0;
   a.plan = nullptr;
   a.nslot = 0;
+  a.fuse = 0;
   if (pr.flat_ranges > 0) {   // ragged caches: even split of the batch's valid rows
     int* plan = reinterpret_cast<int*>(pr.ws + decode_flat_record_floats(pr.B, pr.Hq, pr.d, pr.flat_ranges));
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, pr.seq_lens, pr.B, pr.L, pr.window,
@@ -550,9 +587,10 @@ hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
     return hipGetLastError();
   }
   const long long blocks = (long long)a.B * a.Hkv * a.S;
+  a.fuse = a.S == 1 ? 1 : 0;
   hipLaunchKernelGGL((decode_split_kernel<D, D>), dim3((unsigned)blocks), dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.fuse) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.B * a.P)), dim3(64), 0, st, a);
   return hipGetLastError();
 }

@@ -132,7 +132,8 @@ size_t diffattn_prefill_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d
  * already holds that token (the query sits at position L-1 and sees all L rows).
  * Each cache byte is read from HBM once per KV-head group (both heads of every
  * pair in the group share it), split over `num_splits` key ranges whose partial
- * softmax states are merged by a second kernel.
+ * softmax states are merged by a second kernel; with one range per sequence the
+ * first kernel finishes the output itself and the workspace is not touched.
  *   q        device [B, Hq, d]       (dtype)
  *   k_cache  device [B, L, Hkv, d]   (dtype)
  *   v_cache  device [B, L, Hkv, d]   (dtype)
