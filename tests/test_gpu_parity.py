@@ -141,6 +141,23 @@ def test_decode_edges(gpu_device, B, L, Hq, Hkv, d, splits):
     assert_parity(got, ref, f"decode edge {B,L,Hq,Hkv,d,splits}")
 
 
+@pytest.mark.parametrize("B,L,Hq,Hkv,d", [(3, 300, 32, 2, 64), (2, 77, 16, 1, 128), (4, 1000, 64, 8, 128)])
+def test_decode_one_range_per_sequence(gpu_device, B, L, Hq, Hkv, d):
+    """With one key range per sequence the split kernel finishes o1 - lambda o2 (and the
+    V1 RMSNorm) itself, without records or the combine: G up to 8 (all 16 lane columns
+    of the wave) and d = 64, against the oracle and against the same decode over 4 ranges."""
+    w = W.Workload("one_range", "decode", "bf16", B=B, T=L, Hq=Hq, Hkv=Hkv, d=d, seed=300 + L)
+    got, ref = _decode_case(w, gpu_device, splits=1)
+    assert_parity(got, ref, f"decode one range {B, L, Hq, Hkv, d}")
+    got4, _ = _decode_case(w, gpu_device, splits=4)
+    assert np.abs(got - got4).max() < 1e-2
+    vec = W.make_v1_lambda_vectors(w.P)
+    lam1 = np.ascontiguousarray(np.broadcast_to(
+        oracle.v1_lambda(vec["lq1"], vec["lk1"], vec["lq2"], vec["lk2"], 0.8), (w.B, w.P)), dtype=np.float32)
+    got, ref = _decode_case(w, gpu_device, splits=1, v1=True, eps=1e-5, lam=lam1)
+    assert_parity(got, ref, f"decode one range {B, L, Hq, Hkv, d} V1 mode")
+
+
 def test_decode_fp32(gpu_device):
     w = W.Workload("d32", "decode", "fp32", B=2, T=300, Hq=8, Hkv=2, d=64, seed=8)
     got, ref = _decode_case(w, gpu_device)
