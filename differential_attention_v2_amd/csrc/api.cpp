@@ -24,11 +24,19 @@ constexpr int kDecodeTargetWaves = 512;
 
 bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The kernels address the rows of a tile (up to 64 tokens) with 32-bit per-lane
+// byte offsets from a 64-bit tile base, so 64 token strides of the widest row
+// (q: Hq*d bf16 or fp32 values) must stay below 2^31 bytes.
+constexpr long long kMaxHeadElems = 1LL << 22;   // Hq*d per token
+constexpr int kMaxBackwardT = 1 << 26;
+constexpr int kMaxModelDim = 1 << 24;            // lambda producer: 16 rows of x per 32-bit offset range
+
 int check_heads(int Hq, int Hkv, int d) {
   if (Hkv < 1 || Hq < 2 || Hq % (2 * Hkv) != 0) return DIFFATTN_ERR_INVALID_ARG;
   if (d <= 0) return DIFFATTN_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return DIFFATTN_ERR_UNSUPPORTED;
   if (Hq / (2 * Hkv) > 8) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((long long)Hq * d > kMaxHeadElems) return DIFFATTN_ERR_UNSUPPORTED;
   return DIFFATTN_OK;
 }
 
@@ -137,6 +145,9 @@ int diffattn_prefill_bwd(const void* q, const void* k, const void* v, const floa
     if (!aligned(p16, 16)) return DIFFATTN_ERR_INVALID_ARG;
   if (!aligned(lambda, 4) || !aligned(lse, 4) || !aligned(dlambda, 4)) return DIFFATTN_ERR_INVALID_ARG;
   if (!fits(B, T, Hq, d) || (long long)B * T * (Hq / 2) > kMaxGrid) return DIFFATTN_ERR_INVALID_ARG;
+  // the dK/dV kernel reads the row statistics (5 fields of Tpad floats per pair)
+  // through 32-bit per-lane offsets
+  if (T > kMaxBackwardT) return DIFFATTN_ERR_UNSUPPORTED;
   const size_t need = backward_workspace_floats(B, T, Hq, Hkv, d) * sizeof(float);
   if (!aligned(workspace, 16) || workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
   BackwardProblem p{q, k, v, lambda, out, o2, lse, dout, dq, dk, dv, dlambda, static_cast<float*>(workspace),
@@ -234,7 +245,9 @@ int diffattn_decode_fwd_varlen(const void* q, const void* k_cache, const void* v
 }
 
 size_t diffattn_decode_compare_workspace_bytes(int B, int L, int H, int Hkv, int d, int num_splits) {
-  if (B < 1 || L < 1 || Hkv < 1 || H < 1 || H % Hkv != 0 || H / Hkv > 16 || (d != 64 && d != 128)) return 0;
+  if (B < 1 || L < 1 || Hkv < 1 || H < 1 || H % Hkv != 0 || H / Hkv > 16 || (d != 64 && d != 128) ||
+      (long long)H * d > kMaxHeadElems)
+    return 0;
   int S, chunk;
   if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return 0;
   return 2 * (size_t)B * H * S * decode_record_floats(d) * sizeof(float);
@@ -246,7 +259,7 @@ int decode_compare(const void* q, const void* k_cache, const void* v_cache, cons
                    void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 1 || L < 1 || num_splits < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return DIFFATTN_ERR_INVALID_ARG;
   if (d <= 0) return DIFFATTN_ERR_INVALID_ARG;
-  if ((d != 64 && d != 128) || H / Hkv > 16) return DIFFATTN_ERR_UNSUPPORTED;
+  if ((d != 64 && d != 128) || H / Hkv > 16 || (long long)H * d > kMaxHeadElems) return DIFFATTN_ERR_UNSUPPORTED;
   int st = check_mode(DIFFATTN_BF16, flags, rms_eps);
   if (st) return st;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
@@ -279,7 +292,7 @@ int diffattn_decode_v1_layout(const void* q, const void* k_cache, const void* v_
 int diffattn_lambda_proj(const void* x, const void* w_lambda, float* lambda_out, int rows, int d_model, int P,
                          void* stream) {
   if (rows < 1 || d_model < 1 || P < 1) return DIFFATTN_ERR_INVALID_ARG;
-  if (d_model % 512 != 0 || P % 16 != 0 || P > 64) return DIFFATTN_ERR_UNSUPPORTED;
+  if (d_model % 512 != 0 || d_model > kMaxModelDim || P % 16 != 0 || P > 64) return DIFFATTN_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(w_lambda, 16) || !aligned(lambda_out, 4)) return DIFFATTN_ERR_INVALID_ARG;
   if (!fits(rows, d_model, 1, 1) || !fits(rows, P, 1, 1)) return DIFFATTN_ERR_INVALID_ARG;
   return hip_status(launch_lambda_proj(x, w_lambda, lambda_out, rows, d_model, P, static_cast<hipStream_t>(stream)));

@@ -28,7 +28,9 @@
  *   - Element types: dtype DIFFATTN_BF16 (q/k/v/out are bf16, fp32 accumulation)
  *     or DIFFATTN_FP32 (q/k/v/out are fp32).  lambda is always fp32.
  *   - Layouts are row-major with the head dim fastest ("BTHD").
- *   - Supported: d in {64, 128}; Hq a multiple of 2*Hkv; G = Hq/(2*Hkv) <= 8.
+ *   - Supported: d in {64, 128}; Hq a multiple of 2*Hkv; G = Hq/(2*Hkv) <= 8;
+ *     Hq*d <= 2^22 per token (tile rows are addressed with 32-bit offsets);
+ *     larger head counts return DIFFATTN_ERR_UNSUPPORTED.
  *   - Errors: arguments are validated on the host before anything is enqueued;
  *     on error nothing is written and a nonzero diffattn_status_t is returned.
  *     Device pointers must be non-NULL and 16-byte aligned.  A failed kernel
@@ -116,8 +118,9 @@ int diffattn_prefill_fwd_train(const void* q, const void* k, const void* v, cons
  * Outputs are fully overwritten and must not alias any input.  dk and dv are
  * summed over query chunks with fp32 atomics, so their last bits can vary from
  * run to run; dq and dlambda are deterministic.
- * Returns a diffattn_status_t; sizes whose dK/dV grid (growing with T^2) would
- * exceed 2^31-1 workgroups return DIFFATTN_ERR_HIP with nothing enqueued.
+ * Returns a diffattn_status_t; T > 2^26 returns DIFFATTN_ERR_UNSUPPORTED, and
+ * sizes whose dK/dV grid (growing with T^2) would exceed 2^31-1 workgroups return
+ * DIFFATTN_ERR_HIP with nothing enqueued.
  */
 int diffattn_prefill_bwd(const void* q, const void* k, const void* v, const float* lambda, const void* out,
                          const void* o2, const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -229,7 +232,7 @@ int diffattn_v1_lambda(const float* lq1, const float* lk1, const float* lq2, con
  *   x          device [rows, d_model] bf16 (rows = B*T: the attention block's input)
  *   w_lambda   device [P, d_model] bf16, one projection vector per pair
  *   lambda_out device [rows, P] fp32 -- the `lambda` input of the prefill calls
- * Constraints: d_model % 512 == 0, P % 16 == 0, P <= 64.
+ * Constraints: d_model % 512 == 0, d_model <= 2^24, P % 16 == 0, P <= 64.
  * Returns a diffattn_status_t.
  */
 int diffattn_lambda_proj(const void* x, const void* w_lambda, float* lambda_out, int rows, int d_model, int P,
