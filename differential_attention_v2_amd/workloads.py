@@ -265,3 +265,32 @@ def plant_signal(w: Workload, inputs: dict, probes_per_pair: int = 8, n_signal: 
     inputs["k"] = k
     inputs["plan"] = plan
     return inputs
+
+
+def signal_indicator_v(w: Workload, plan: list) -> tuple[np.ndarray, dict]:
+    """Value rows that make a prefill's output read out attention mass directly.
+
+    For the signal-plus-noise variant's plan (from ``plant_signal``): within each
+    (b, KV head g), probe number c (in plan order) owns column c of V, which is 1
+    on that probe's planted key rows and 0 elsewhere; column ``n_probes`` is 1 on
+    every row; all other columns are 0.  With these values, output column c of the
+    probe's own row and pair is the mass its attention map puts on the planted
+    keys, and the all-ones column is the map's row sum.  Returns (v as bf16 bits
+    [B, T, Hkv, d], {(b, p, row): column}) and requires more columns than probes
+    per KV head.
+    """
+    assert w.kind == "prefill"
+    v = np.zeros((w.B, w.T, w.Hkv, w.d), dtype=np.uint16)
+    one = np.uint16(0x3F80)           # bf16 1.0
+    column, count = {}, {}
+    for b, p, i, pos in plan:
+        g = p // w.G
+        c = count.get((b, g), 0)
+        count[(b, g)] = c + 1
+        v[b, pos, g, c] = one
+        column[(b, p, i)] = c
+    ones_col = max(count.values())
+    assert ones_col < w.d, "more probes per KV head than value columns"
+    v[:, :, :, ones_col] = one
+    column["ones"] = ones_col
+    return v, column

@@ -6,7 +6,7 @@ import os
 import numpy as np
 
 from differential_attention_v2_amd.workloads import Workload
-from oracle import diffattn_decode, v1_lambda
+from oracle import attention_weights, diffattn_decode, snr, v1_lambda
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_values.json")))
 
@@ -38,6 +38,22 @@ def test_v2_kv_cache_equals_baseline_gqa():
     assert v2.decode_kv_bytes() == base.decode_kv_bytes() == 2 * 4096 * 8 * 128 * 2
 
 
-def test_toy_gain_range_constants():
+def test_toy_gain_range_through_the_oracle():
+    """The printed 3x-10x SNR gain of differential over softmax attention, reproduced
+    through the oracle on the toy's rows (16 keys at 4 q/|q| among N(0, 1) keys, the
+    branches' queries independent) in the long-context regime, for lambda from 0.7 to
+    0.85, where the gain (about 1/(1 - lambda)) spans the printed range."""
     t = GOLD["toy_snr_gain"]
-    assert (t["low"], t["high"]) == (3.0, 10.0)
+    rng = np.random.default_rng(2024)
+    N, d = 32768, 128
+    gains = []
+    for lam in (0.7, 0.75, 0.8, 0.85):
+        q1, q2 = rng.standard_normal(d) / math.sqrt(2), rng.standard_normal(d) / math.sqrt(2)
+        k = rng.standard_normal((N, d))
+        pos = rng.choice(N, 16, replace=False)
+        k[pos] = 4 * q1 / np.linalg.norm(q1)
+        a1 = attention_weights(q1[None], k, np.array([N - 1]), False)[0]
+        a2 = attention_weights(q2[None], k, np.array([N - 1]), False)[0]
+        gains.append(snr(a1 - lam * a2, pos, N) / snr(a1, pos, N))
+    assert all(t["low"] <= g <= t["high"] for g in gains), gains
+    assert gains == sorted(gains)

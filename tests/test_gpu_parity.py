@@ -57,8 +57,10 @@ def test_prefill_T4096_all_rows(gpu_device):
 
 
 def _sampled_rows(T, seed=3):
+    """First and last 128 rows, both rows at every 64-token key-tile boundary below
+    4096 and at every 4096th token, and 256 uniform random rows."""
     rng = np.random.default_rng(seed)
-    edges = np.concatenate([[t - 1, t] for t in range(64, T, 4096)])
+    edges = np.concatenate([[t - 1, t] for t in list(range(64, min(T, 4096), 64)) + list(range(4096, T, 4096))])
     rows = np.concatenate([np.arange(128), np.arange(T - 128, T), edges, rng.choice(T, 256, replace=False)])
     return np.unique(rows[(rows >= 0) & (rows < T)])
 
@@ -70,26 +72,52 @@ def test_prefill_T32768_sampled_rows(gpu_device):
     assert_parity(got, ref, f"bf16 prefill T=32768 ({rows.size} sampled rows, all pairs)")
 
 
-def test_decode_B64_L8192(gpu_device):
+def _decode_refs_per_sequence(w: W.Workload, inp: dict, modes: list) -> list:
+    """The fp64 oracle on every (b, pair) output of a decode workload, for each
+    (lambda [B, P], v1, eps) mode.  The cache is widened to fp64 one sequence at a
+    time (a B=8, L=131072 bf16 cache would be 17 GB as a whole)."""
+    refs = [np.empty((w.B, w.P, w.d)) for _ in modes]
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        q, k, v = (_f64(inp[n][sl], w.dtype) for n in ("q", "k", "v"))
+        for ref, (lam, v1, eps) in zip(refs, modes):
+            ref[b] = oracle.diffattn_decode(q, k, v, lam[sl], v1_rmsnorm=v1, eps=eps)[0]
+    return refs
+
+
+def _decode_gpu(w: W.Workload, inp: dict, dev, lam, v1=False, eps=1e-5, splits=0):
+    q, k, v = (to_device(inp[n], w.dtype, dev) for n in ("q", "k", "v"))
+    lam_t = torch.from_numpy(np.ascontiguousarray(lam, dtype=np.float32)).to(dev)
+    return from_device(bd.decode(q, k, v, lam_t, v1_rmsnorm=v1, eps=eps, num_splits=splits))
+
+
+def test_decode_B64_L8192_all_sequences(gpu_device):
+    """Every (b, pair) output of the B=64, L=8192 decode (one key range per sequence:
+    the split kernel writes the output itself), V2 map."""
     w = W.DECODE_B64_L8192
-    got, ref = _decode_case(w, gpu_device, batches=[0, 1, 13, 31, 32, 47, 62, 63])
-    assert_parity(got, ref, "decode B=64 L=8192 (8 batches, all pairs)")
+    inp = W.make_decode(w)
+    got = _decode_gpu(w, inp, gpu_device, inp["lam"])
+    (ref,) = _decode_refs_per_sequence(w, inp, [(inp["lam"], False, 1e-5)])
+    assert_parity(got, ref, f"decode B={w.B} L={w.T} (all {w.B} x {w.P} outputs)")
 
 
-def test_decode_B8_L131072_and_v1_mode(gpu_device):
+def test_decode_B8_L131072_and_v1_mode_all_outputs(gpu_device):
+    """Every (b, pair) output of the B=8, L=131072 decode (8 key ranges per sequence and
+    the combine kernel), in V2 mode and in V1 reference mode (exp-dot lambda from the
+    library's own kernel, RMSNorm eps = 1e-5)."""
     w = W.DECODE_B8_L131072
-    b, p = [0, 5], [0, 9, 18, 31]
-    got, ref = _decode_case(w, gpu_device, batches=b, pairs=p)
-    assert_parity(got, ref, "decode B=8 L=131072")
+    inp = W.make_decode(w)
     vec = W.make_v1_lambda_vectors(w.P)
     lam1 = oracle.v1_lambda(vec["lq1"], vec["lk1"], vec["lq2"], vec["lk2"], 0.8)
     # the V1 lambda through the library's own kernel, checked against the oracle
     dv = {n: torch.from_numpy(vec[n]).to(gpu_device) for n in vec}
-    lam_dev = bd.v1_lambda(dv["lq1"], dv["lk1"], dv["lq2"], dv["lk2"], 0.8, rows=w.B)
-    np.testing.assert_allclose(lam_dev.cpu().numpy(), np.broadcast_to(lam1, (w.B, w.P)), rtol=2e-6, atol=2e-6)
-    got, ref = _decode_case(w, gpu_device, batches=b, pairs=p, v1=True, eps=1e-5,
-                            lam=lam_dev.cpu().numpy())
-    assert_parity(got, ref, "decode B=8 L=131072 V1 mode (exp-dot lambda, RMSNorm eps=1e-5)")
+    lam_dev = bd.v1_lambda(dv["lq1"], dv["lk1"], dv["lq2"], dv["lk2"], 0.8, rows=w.B).cpu().numpy()
+    np.testing.assert_allclose(lam_dev, np.broadcast_to(lam1, (w.B, w.P)), rtol=2e-6, atol=2e-6)
+    got2 = _decode_gpu(w, inp, gpu_device, inp["lam"])
+    got1 = _decode_gpu(w, inp, gpu_device, lam_dev, v1=True, eps=1e-5)
+    ref2, ref1 = _decode_refs_per_sequence(w, inp, [(inp["lam"], False, 1e-5), (lam_dev, True, 1e-5)])
+    assert_parity(got2, ref2, f"decode B={w.B} L={w.T} (all {w.B} x {w.P} outputs)")
+    assert_parity(got1, ref1, f"decode B={w.B} L={w.T} V1 mode (exp-dot lambda, RMSNorm eps=1e-5; all outputs)")
 
 
 # ------------------------------------------------------------------ edge shapes

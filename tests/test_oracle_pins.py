@@ -275,6 +275,19 @@ def _toy_row(rng, N, d, lam):
     return a1, a2, pos
 
 
+def test_snr_absolute_values_worked_by_hand():
+    """Rows worked out by hand (SNR = mean weight on the signal positions over the
+    signed mean weight on the other visible positions)."""
+    # signal {0, 2}: mean 0.3; others {1, 3, 4}: mean 0.4/3; the sixth entry is not visible
+    w = np.array([0.4, 0.1, 0.2, 0.1, 0.2, 0.9])
+    assert snr(w, [0, 2], 5) == pytest.approx(0.3 / (0.4 / 3), rel=1e-15)      # 2.25
+    # a differential row whose unrelated weights average below zero: the SNR is negative
+    w = np.array([0.2, -0.1, 0.05, 0.02])
+    assert snr(w, [0], 4) == pytest.approx(0.2 / (-0.03 / 3), rel=1e-12)         # -20
+    # uniform weights carry no signal: SNR 1
+    assert snr(np.full(10, 0.1), [3, 7], 10) == pytest.approx(1.0, rel=1e-15)
+
+
 @pytest.mark.parametrize("N", [1024, 32768])
 def test_snr_identity_from_row_sums(N):
     """SNR_diff/SNR_std = ((s1 - lam s2)/s1) (1 - s1) / ((1 - s1) - lam (1 - s2)) with s_r = signal mass."""
