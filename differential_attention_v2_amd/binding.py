@@ -346,8 +346,9 @@ def output_proj(attn, w_o, out=None, stream=None):
     return out
 
 
-def prefill_train(q, k, v, lam, causal: bool = True, stream=None):
-    """(out, o2, lse) of the bf16 training forward: out [B,T,P,d], o2 [B,T,P,d], lse [B,T,Hq] fp32."""
+def prefill_train(q, k, v, lam, causal: bool = True, out=None, stream=None):
+    """(out, o2, lse) of the bf16 training forward: out [B,T,P,d], o2 [B,T,P,d], lse [B,T,Hq] fp32.
+    `out` may pass the three output tensors to fill."""
     torch = _torch()
     B, T, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -355,9 +356,14 @@ def prefill_train(q, k, v, lam, causal: bool = True, stream=None):
     _check(k, "k", (B, T, Hkv, d), torch.bfloat16)
     _check(v, "v", (B, T, Hkv, d), torch.bfloat16)
     _check(lam, "lam", (B, T, Hq // 2), torch.float32)
-    out = torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device)
-    o2 = torch.empty_like(out)
-    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = (torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device),
+               torch.empty((B, T, Hq // 2, d), dtype=q.dtype, device=q.device),
+               torch.empty((B, T, Hq), dtype=torch.float32, device=q.device))
+    out, o2, lse = out
+    _check(out, "out", (B, T, Hq // 2, d), torch.bfloat16)
+    _check(o2, "o2", (B, T, Hq // 2, d), torch.bfloat16)
+    _check(lse, "lse", (B, T, Hq), torch.float32)
     st = diffattn_prefill_fwd_train(q.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(), out.data_ptr(),
                                     o2.data_ptr(), lse.data_ptr(), B, T, Hq, Hkv, d, int(bool(causal)),
                                     _stream(stream))
