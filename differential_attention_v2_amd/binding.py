@@ -23,6 +23,7 @@ DIFFATTN_ERR_HIP = 4
 DIFFATTN_BF16 = 0
 DIFFATTN_FP32 = 1
 DIFFATTN_FLAG_V1_RMSNORM = 0x1
+DIFFATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _c_int, _c_uint, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_uint, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -31,6 +32,8 @@ _SIGNATURES = {
                                       _c_int, _c_uint, _c_float, _vp]),
     "diffattn_decode_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, _c_uint, _c_float, _c_int, _vp, _c_size, _vp]),
+    "diffattn_decode_fwd_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _c_int, _c_uint, _c_float, _c_int, _vp]),
     "diffattn_prefill_fwd_window": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_int, _c_uint, _c_float, _vp]),
     "diffattn_decode_fwd_varlen": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -87,6 +90,12 @@ def diffattn_decode_fwd(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, 
                         workspace, workspace_bytes, stream):
     return load_library().diffattn_decode_fwd(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, flags,
                                               rms_eps, num_splits, workspace, workspace_bytes, stream)
+
+
+def diffattn_decode_fwd_noalloc(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, flags, rms_eps, num_splits,
+                                stream):
+    return load_library().diffattn_decode_fwd_noalloc(q, k_cache, v_cache, lam, out, B, L, Hq, Hkv, d, dtype, flags,
+                                                      rms_eps, num_splits, stream)
 
 
 def diffattn_prefill_fwd_window(q, k, v, lam, out, B, T, Hq, Hkv, d, window, dtype, flags, rms_eps, stream):

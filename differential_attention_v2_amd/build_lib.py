@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip", "backward_bf16.hip", "proj_bf16.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip", "backward_bf16.hip", "proj_bf16.hip",
+           "noalloc_scratch.hip"]
 # the output projection is a plain GEMM run by rocBLAS
 LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 

@@ -197,6 +197,30 @@ int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
   return hip_status(launch_decode_bf16(p, s));
 }
 
+int diffattn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
+                                void* out, int B, int L, int Hq, int Hkv, int d, int dtype, unsigned flags,
+                                float rms_eps, int num_splits, void* stream) {
+  // the records' size is known only for a valid problem: validate like the
+  // workspace entry point first, with a workspace that is never touched
+  if (B < 1 || L < 1 || num_splits < 0) return DIFFATTN_ERR_INVALID_ARG;
+  int st = check_heads(Hq, Hkv, d);
+  if (st) return st;
+  st = check_mode(dtype, flags, rms_eps);
+  if (st) return st;
+  int S, chunk;
+  if (!decode_plan(B, L, Hkv, num_splits, &S, &chunk)) return DIFFATTN_ERR_INVALID_ARG;
+  if (!fits(B, Hq, S, decode_record_floats(d)) ||
+      (size_t)B * Hq * S * decode_record_floats(d) * sizeof(float) > DIFFATTN_NOALLOC_SCRATCH_BYTES)
+    return DIFFATTN_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(lambda, 4))
+    return DIFFATTN_ERR_INVALID_ARG;
+  void* scratch = nullptr;
+  if (decode_scratch(&scratch) != hipSuccess) return DIFFATTN_ERR_HIP;
+  return diffattn_decode_fwd(q, k_cache, v_cache, lambda, out, B, L, Hq, Hkv, d, dtype, flags, rms_eps, num_splits,
+                             scratch, DIFFATTN_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 namespace {
 // ranges per KV head of the even split over ragged caches: the same wave target
 int varlen_ranges(int Hkv, int num_splits) {

@@ -104,6 +104,9 @@ hipError_t launch_prefill_bf16(const PrefillProblem& p, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeProblem& p, hipStream_t s);
 hipError_t launch_backward_bf16(const BackwardProblem& p, hipStream_t s);
 hipError_t launch_decode_compare_bf16(const CompareProblem& p, hipStream_t s);
+// Device address of the current device's fixed decode scratch
+// (DIFFATTN_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned).
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_lambda_proj(const void* x, const void* w, float* lam, int rows, int dm, int P, hipStream_t s);
 // 0 on success
 int run_output_proj(const void* attn, const void* w_o, void* y, int rows, int in_dim, int out_dim, hipStream_t s);

@@ -154,6 +154,32 @@ int diffattn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and kernels as diffattn_decode_fwd
+ * minus the workspace: the key-range records live in a fixed device array of
+ * DIFFATTN_NOALLOC_SCRATCH_BYTES bytes inside the library, one per device, held
+ * from the first call on that device until the process ends.  The call never
+ * allocates or frees device memory.
+ *   - Problems whose records need more than DIFFATTN_NOALLOC_SCRATCH_BYTES
+ *     (B * Hq * splits * (d + 4) * 4 bytes when splits > 1) return
+ *     DIFFATTN_ERR_WORKSPACE with nothing enqueued; use diffattn_decode_fwd.
+ *   - Every call on a device shares that device's array: calls that overlap in
+ *     time on one device (different streams, or threads without ordering) race
+ *     and may corrupt each other's output.  Calls ordered on one stream are safe.
+ *   - The array keeps the last call's records; nothing in it needs to start at
+ *     zero, since each call writes every record it reads.
+ *   - The first call on a device looks up the array's device address (a HIP
+ *     runtime call, DIFFATTN_ERR_HIP on failure) and must run with that device
+ *     current; make that first call outside graph capture.
+ * Returns a diffattn_status_t.
+ */
+#define DIFFATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int diffattn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache, const float* lambda,
+                                void* out, int B, int L, int Hq, int Hkv, int d,
+                                int dtype, unsigned flags, float rms_eps, int num_splits, void* stream);
+
+/*
  * Decode over ragged caches: sequence b holds seq_lens[b] valid rows of a cache
  * allocated for L (its query is the token at row seq_lens[b]-1), and with
  * window > 0 only its last `window` rows are visible.  Serving engines batch

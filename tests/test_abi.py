@@ -275,3 +275,25 @@ def test_backward_sequence_limit(lib):
 
 def test_lambda_proj_model_dim_limit(lib):
     assert bd.diffattn_lambda_proj(P, P, P, 16, (1 << 24) + 512, 32, None) == bd.DIFFATTN_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_validation(lib):
+    """The decode entry point without a workspace validates on the host like the
+    workspace one and refuses problems whose records exceed its fixed array."""
+    text = open(HEADER).read()
+    m = re.search(r"#define DIFFATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == bd.DIFFATTN_NOALLOC_SCRATCH_BYTES
+
+    def call(**kw):
+        a = dict(q=P, k_cache=P, v_cache=P, lam=P, out=P, B=2, L=100, Hq=8, Hkv=2, d=128, dtype=0, flags=0,
+                 rms_eps=1e-5, num_splits=0, stream=None)
+        a.update(kw)
+        return bd.diffattn_decode_fwd_noalloc(**a)
+
+    assert call(B=0) == bd.DIFFATTN_ERR_INVALID_ARG
+    assert call(q=None) == bd.DIFFATTN_ERR_INVALID_ARG
+    assert call(out=P + 8) == bd.DIFFATTN_ERR_INVALID_ARG
+    assert call(d=96) == bd.DIFFATTN_ERR_UNSUPPORTED
+    assert call(flags=1, rms_eps=0.0) == bd.DIFFATTN_ERR_INVALID_ARG
+    # 64 x 64 heads x 64 ranges x (128 + 4) floats = 138 MB of records > 32 MiB
+    assert call(B=64, L=8192, Hq=64, Hkv=8, num_splits=64) == bd.DIFFATTN_ERR_WORKSPACE
