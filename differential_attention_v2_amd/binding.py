@@ -13,7 +13,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdiffattn.so")
+# DIFFATTN_LIBRARY may name another build of the same library (for example a
+# sanitizer build of the host layer); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("DIFFATTN_LIBRARY") or os.path.join(PKG, "libdiffattn.so")
 
 DIFFATTN_OK = 0
 DIFFATTN_ERR_INVALID_ARG = 1
