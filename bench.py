@@ -42,8 +42,8 @@ METRIC = "DiffAttn-V2 fwd: prefill TFLOP/s & decode KV GB/s, % of MI355X peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SECTIONS = ("main", "short", "backward", "serving", "layouts", "projections", "snr")
 BACKWARD_KERNELS = "bwd_pre + fill_zero + bwd_dkdv_kernel<128> + bwd_dq_kernel<128> + 2 x convert"
-OUTPUT_PROJ_ENGINES = {"output_proj": "rocBLAS gemm_ex (bf16, fp32 accumulate)",
-                       "output_proj_rocblas": "rocBLAS gemm_ex (bf16, fp32 accumulate)"}
+OUTPUT_PROJ_ENGINES = {"output_proj": "gemm_bf16_kernel (this library: 256x256 tiles, bf16 MFMA, fp32 accumulate)",
+                       "output_proj_library": "torch.matmul (hipBLASLt, bf16, fp32 accumulate): baseline"}
 
 
 def _kernel_hash(files):
@@ -437,8 +437,9 @@ def main() -> int:
         jy = torch.empty((rows, dm), dtype=torch.bfloat16, device=dev)
         jruns = {"lambda_proj": lambda: bd.lambda_proj(jx, jw, out=jl),
                  "output_proj": lambda: bd.output_proj(ja, jo, out=jy)}
-        if hasattr(bd, "output_proj_rocblas"):
-            jruns["output_proj_rocblas"] = lambda: bd.output_proj_rocblas(ja, jo, out=jy)
+        # the same product by torch's library GEMM (hipBLASLt), as a baseline
+        jy2 = torch.empty_like(jy)
+        jruns["output_proj_library"] = lambda: torch.matmul(ja, jo, out=jy2)
         jt = {}
         for name, fn in jruns.items():
             settle(fn, min(args.settle_ms, 100.0))
@@ -451,7 +452,7 @@ def main() -> int:
                                 "ms_per_launch": jt["lambda_proj"], "algorithmic_bytes_per_launch": lp_bytes,
                                 "frac": lp_bytes / (jt["lambda_proj"] * 1e-3) / 1e9 / PEAK_HBM_GBS, "bound": "hbm",
                                 "workload": f"x [{rows}, {dm}] bf16, w [{w2.P}, {dm}] -> lambda [{rows}, {w2.P}] fp32"}}
-        for name in ("output_proj", "output_proj_rocblas"):
+        for name in ("output_proj", "output_proj_library"):
             if name in jt:
                 tf = op_flops / (jt[name] * 1e-3) / 1e12
                 proj[name] = {"value": tf, "unit": "TFLOP/s", "ms_per_launch": jt[name],
@@ -459,7 +460,7 @@ def main() -> int:
                               "bound": "mfma", "engine": OUTPUT_PROJ_ENGINES[name],
                               "workload": f"[{rows}, {kin}] x [{kin}, {dm}] bf16"}
         res["projections"] = proj
-        del jx, jw, ja, jo, jl, jy
+        del jx, jw, ja, jo, jl, jy, jy2
         torch.cuda.empty_cache()
 
     # ---- signal-plus-noise SNR from the device's outputs --------------------------------

@@ -342,7 +342,8 @@ def lambda_proj(x, w_lambda, out=None, stream=None):
 
 
 def output_proj(attn, w_o, out=None, stream=None):
-    """y [rows, out_dim] = attn [rows, in_dim] @ w_o [in_dim, out_dim], bf16 (rocBLAS inside the library)."""
+    """y [rows, out_dim] = attn [rows, in_dim] @ w_o [in_dim, out_dim], bf16 (the library's MFMA GEMM;
+    in_dim % 32 == 0, out_dim % 8 == 0)."""
     torch = _torch()
     rows, kin = attn.shape
     nout = w_o.shape[1]

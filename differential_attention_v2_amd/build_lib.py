@@ -23,9 +23,8 @@ LIB = os.path.join(PKG, "libdiffattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "rows_f32.hip", "backward_bf16.hip", "proj_bf16.hip",
-           "noalloc_scratch.hip"]
-# the output projection is a plain GEMM run by rocBLAS
-LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+           "gemm_bf16.hip", "noalloc_scratch.hip"]
+LIBS = []
 
 # Packed-fp32 VALU instructions are kept out of every kernel; hipcc -O3 would
 # otherwise form them from plain float code.

@@ -325,12 +325,14 @@ int diffattn_lambda_proj(const void* x, const void* w_lambda, float* lambda_out,
 int diffattn_output_proj(const void* attn, const void* w_o, void* y, int rows, int in_dim, int out_dim,
                          void* stream) {
   if (rows < 1 || in_dim < 1 || out_dim < 1) return DIFFATTN_ERR_INVALID_ARG;
+  // 32-wide k steps and 16-byte column chunks; 256 rows (32 k-rows) of the
+  // operands are addressed with 32-bit per-lane offsets
+  if (in_dim % 32 != 0 || out_dim % 8 != 0 || in_dim > kMaxModelDim || out_dim > kMaxModelDim)
+    return DIFFATTN_ERR_UNSUPPORTED;
   if (!aligned(attn, 16) || !aligned(w_o, 16) || !aligned(y, 16)) return DIFFATTN_ERR_INVALID_ARG;
   if (!fits(rows, in_dim, 1, 1) || !fits(in_dim, out_dim, 1, 1) || !fits(rows, out_dim, 1, 1))
     return DIFFATTN_ERR_INVALID_ARG;
-  return run_output_proj(attn, w_o, y, rows, in_dim, out_dim, static_cast<hipStream_t>(stream)) == 0
-             ? DIFFATTN_OK
-             : DIFFATTN_ERR_HIP;
+  return hip_status(launch_gemm_bf16(attn, w_o, y, rows, out_dim, in_dim, static_cast<hipStream_t>(stream)));
 }
 
 int diffattn_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2, float lambda_init,

@@ -108,8 +108,8 @@ hipError_t launch_decode_compare_bf16(const CompareProblem& p, hipStream_t s);
 // (DIFFATTN_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned).
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_lambda_proj(const void* x, const void* w, float* lam, int rows, int dm, int P, hipStream_t s);
-// 0 on success
-int run_output_proj(const void* attn, const void* w_o, void* y, int rows, int in_dim, int out_dim, hipStream_t s);
+// y [M, N] = a [M, K] @ w [K, N], row-major bf16, fp32 accumulation; K % 32 == 0, N % 8 == 0.
+hipError_t launch_gemm_bf16(const void* a, const void* w, void* y, int M, int N, int K, hipStream_t s);
 // fp32 path: rows of queries [B, Tq] over Tk keys; causal limit j <= i + (Tk - Tq).
 hipError_t launch_rows_f32(const PrefillProblem& p, int Tq, int Tk, hipStream_t s);
 hipError_t launch_v1_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,

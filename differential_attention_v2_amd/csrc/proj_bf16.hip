@@ -1,4 +1,4 @@
-// The projections on either side of the V2 attention core, gfx950.
+// The lambda producer in front of the V2 attention core, gfx950.
 //
 // lambda producer: V2 projects a sigmoid-bounded lambda for every token and head
 // (dailytechsnack.ch article "Differential Transformer V2 soll KI-Training
@@ -11,12 +11,7 @@
 // LDS and the sigmoid is applied in fp32.  x is read from HBM exactly once; w
 // (P x d_model, 256 KB for P = 32, d_model = 4096) stays in L2.
 //
-// Output projection: after the subtraction the P*d wide result is projected back
-// to d_model by O_W (differential-attention lesson "差异性注意力 (V2)", section
-// "V1 vs V2") -- a plain dense GEMM, run by rocBLAS (bf16 in and out, fp32
-// accumulation).
-#include <rocblas/rocblas.h>
-
+// The output projection O_W on the other side is the GEMM in gemm_bf16.hip.
 #include "dev_common.h"
 #include "internal.h"
 
@@ -121,16 +116,6 @@ __global__ __launch_bounds__(64 * LP_WAVES) void lambda_proj_kernel(const bf16* 
   }
 }
 
-// One rocBLAS handle per (thread, device), created on first use.
-rocblas_handle blas_handle() {
-  constexpr int kMaxDevices = 64;
-  thread_local rocblas_handle handles[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  if (handles[dev] == nullptr && rocblas_create_handle(&handles[dev]) != rocblas_status_success) handles[dev] = nullptr;
-  return handles[dev];
-}
-
 }  // namespace
 
 hipError_t launch_lambda_proj(const void* x, const void* w, float* lam, int rows, int dm, int P, hipStream_t s) {
@@ -144,22 +129,6 @@ hipError_t launch_lambda_proj(const void* x, const void* w, float* lam, int rows
     default: hipLaunchKernelGGL(lambda_proj_kernel<4>, grid, block, 0, s, xb, wb, lam, rows, dm); break;
   }
   return hipGetLastError();
-}
-
-// y [rows, out_dim] = attn [rows, in_dim] @ w_o [in_dim, out_dim], row-major bf16.
-// In rocBLAS's column-major terms: y^T (out_dim x rows) = w_o^T (out_dim x in_dim)
-// * attn^T (in_dim x rows), with each row-major matrix read as its transpose.
-int run_output_proj(const void* attn, const void* w_o, void* y, int rows, int in_dim, int out_dim, hipStream_t s) {
-  rocblas_handle h = blas_handle();
-  if (h == nullptr) return 1;
-  if (rocblas_set_stream(h, s) != rocblas_status_success) return 1;
-  const float alpha = 1.0f, beta = 0.0f;
-  const rocblas_status st =
-      rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, out_dim, rows, in_dim, &alpha, w_o,
-                      rocblas_datatype_bf16_r, out_dim, attn, rocblas_datatype_bf16_r, in_dim, &beta, y,
-                      rocblas_datatype_bf16_r, out_dim, y, rocblas_datatype_bf16_r, out_dim,
-                      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  return st == rocblas_status_success ? 0 : 1;
 }
 
 }  // namespace diffattn

@@ -269,9 +269,11 @@ int diffattn_lambda_proj(const void* x, const void* w_lambda, float* lambda_out,
  * model width (differential-attention lesson, section "V1 vs V2").
  *   y [rows, out_dim] = attn [rows, in_dim] @ w_o [in_dim, out_dim], all bf16
  *   row-major, fp32 accumulation; attn is the prefill's out viewed as [B*T, P*d].
- * A plain dense GEMM, run by rocBLAS on `stream`; the library keeps one rocBLAS
- * handle per calling thread and device (created on first use; rocBLAS may keep
- * its own device workspace).  Returns a diffattn_status_t.
+ * A dense GEMM on bf16 MFMA (the library's own kernel, 256 x 256 output tiles);
+ * like every entry point here it allocates nothing.
+ * Constraints: in_dim % 32 == 0 and out_dim % 8 == 0 (in_dim = P*d always is a
+ * multiple of 64), both <= 2^24; otherwise DIFFATTN_ERR_UNSUPPORTED.
+ * Returns a diffattn_status_t.
  */
 int diffattn_output_proj(const void* attn, const void* w_o, void* y, int rows, int in_dim, int out_dim,
                          void* stream);

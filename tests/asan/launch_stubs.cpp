@@ -14,7 +14,9 @@ hipError_t launch_decode_compare_bf16(const CompareProblem&, hipStream_t) { retu
 hipError_t launch_lambda_proj(const void*, const void*, float*, int, int, int, hipStream_t) {
   return hipErrorNotSupported;
 }
-int run_output_proj(const void*, const void*, void*, int, int, int, hipStream_t) { return 1; }
+hipError_t launch_gemm_bf16(const void*, const void*, void*, int, int, int, hipStream_t) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_rows_f32(const PrefillProblem&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_v1_lambda(const float*, const float*, const float*, const float*, float, float*, int, int, int,
                             hipStream_t) {

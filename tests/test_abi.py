@@ -237,6 +237,8 @@ def test_lambda_proj_rejects(lib, kw, status):
 
 
 def test_output_proj_rejects(lib):
+    assert bd.diffattn_output_proj(P, P, P, 16, 48, 64, None) == bd.DIFFATTN_ERR_UNSUPPORTED   # k steps of 32
+    assert bd.diffattn_output_proj(P, P, P, 16, 64, 60, None) == bd.DIFFATTN_ERR_UNSUPPORTED   # 16-byte columns
     assert bd.diffattn_output_proj(P, P, None, 16, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
     assert bd.diffattn_output_proj(P, P + 2, P, 16, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
     assert bd.diffattn_output_proj(P, P, P, 0, 64, 64, None) == bd.DIFFATTN_ERR_INVALID_ARG
