@@ -448,6 +448,30 @@ def decode(q, k_cache, v_cache, lam, v1_rmsnorm: bool = False, eps: float = 1e-5
     return out
 
 
+def decode_noalloc(q, k_cache, v_cache, lam, v1_rmsnorm: bool = False, eps: float = 1e-5, num_splits: int = 0,
+                   out=None, stream=None):
+    """decode() without a workspace: the key-range records use the library's fixed
+    per-device scratch (diffattn_decode_fwd_noalloc; calls on one device must not
+    overlap in time)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    L, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _check(q, "q", (B, Hq, d), q.dtype)
+    _check(k_cache, "k_cache", (B, L, Hkv, d), q.dtype)
+    _check(v_cache, "v_cache", (B, L, Hkv, d), q.dtype)
+    _check(lam, "lam", (B, Hq // 2), torch.float32)
+    if out is None:
+        out = torch.empty((B, Hq // 2, d), dtype=q.dtype, device=q.device)
+    _check(out, "out", (B, Hq // 2, d), q.dtype)
+    st = diffattn_decode_fwd_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lam.data_ptr(),
+                                     out.data_ptr(), B, L, Hq, Hkv, d, _dtype_code(q),
+                                     DIFFATTN_FLAG_V1_RMSNORM if v1_rmsnorm else 0, float(eps), int(num_splits),
+                                     _stream(stream))
+    if st != DIFFATTN_OK:
+        raise DiffAttnError(st, "diffattn_decode_fwd_noalloc")
+    return out
+
+
 def v1_lambda(lq1, lk1, lq2, lk2, lambda_init: float, rows: int, out=None, stream=None):
     """lambda [rows, P] = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init per pair, broadcast over rows."""
     torch = _torch()

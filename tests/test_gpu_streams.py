@@ -28,13 +28,20 @@ DEC = W.Workload("stream_decode", "decode", "bf16", B=3, T=1500, Hq=16, Hkv=2, d
 WINDOW = 200
 
 
+# projections either side of the core: lambda from x [T, 512] (16 pairs), O_W of the
+# prefill's output [T, P*d] back to 512
+PROJ_DM, PROJ_P = 512, 16
+
+
 def _host_inputs(seed_offset: int) -> dict:
     pre = W.make_prefill(PRE.with_(seed=PRE.seed + seed_offset))
     dec = W.make_decode(DEC.with_(seed=DEC.seed + seed_offset))
+    proj = W.make_projections(PRE.B * PRE.T, PROJ_DM, PROJ_P, PRE.P * PRE.d, PROJ_DM, seed=9400 + seed_offset)
     return dict(q=pre["q"], k=pre["k"], v=pre["v"], lam=pre["lam"],
                 dout=W.make_dout(PRE.with_(seed=PRE.seed + seed_offset)),
                 qd=dec["q"], kc=dec["k"], vc=dec["v"], lamd=dec["lam"],
-                lens=W.ragged_lengths(DEC.B, DEC.T, seed=9300 + seed_offset))
+                lens=W.ragged_lengths(DEC.B, DEC.T, seed=9300 + seed_offset),
+                xl=proj["x"], wl=proj["w_lambda"], wo=proj["w_o"])
 
 
 def _to_device(h: dict, dev) -> dict:
@@ -61,7 +68,10 @@ def _buffers(dev) -> dict:
                 dv=torch.empty((B, T, Hkv, d), **bf), dlam=torch.empty((B, T, P), dtype=torch.float32, device=dev),
                 ws_dec=bd.decode_workspace(DEC.B, DEC.T, DEC.Hq, DEC.Hkv, DEC.d, device=dev),
                 ws_var=torch.empty(n_var, dtype=torch.uint8, device=dev),
-                ws_bwd=torch.empty(n_bwd, dtype=torch.uint8, device=dev))
+                ws_bwd=torch.empty(n_bwd, dtype=torch.uint8, device=dev),
+                lp=torch.empty((B * T, PROJ_P), dtype=torch.float32, device=dev),
+                y=torch.empty((B * T, PROJ_DM), **bf),
+                dna=torch.empty((DEC.B, DEC.P, DEC.d), **bf))
 
 
 def _run_all(x: dict, o: dict) -> dict:
@@ -73,10 +83,15 @@ def _run_all(x: dict, o: dict) -> dict:
     out, o2, lse = bd.prefill_train(x["q"], x["k"], x["v"], x["lam"])
     bd.prefill_backward(x["q"], x["k"], x["v"], x["lam"], out, o2, lse, x["dout"], workspace=o["ws_bwd"],
                         grads=(o["dq"], o["dk"], o["dv"], o["dlam"]))
+    bd.lambda_proj(x["xl"], x["wl"], out=o["lp"])
+    bd.output_proj(o["pre"].view(PRE.B * PRE.T, PRE.P * PRE.d), x["wo"], out=o["y"])
+    # the decode without a workspace, over 4 key ranges (its records go through the
+    # library's fixed scratch); its first call on the device ran before any capture
+    bd.decode_noalloc(x["qd"], x["kc"], x["vc"], x["lamd"], num_splits=4, out=o["dna"])
     return dict(train_out=out, o2=o2, lse=lse)
 
 
-RESULTS = ("pre", "win", "dec", "var", "dq", "dk", "dv", "dlam")
+RESULTS = ("pre", "win", "dec", "var", "dq", "dk", "dv", "dlam", "lp", "y", "dna")
 ATOMIC = ("dk", "dv")
 
 
