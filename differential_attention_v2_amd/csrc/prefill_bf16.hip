@@ -11,24 +11,27 @@
 //
 // Work decomposition.  A workgroup of 8 waves (two per SIMD) owns one (batch b,
 // KV head g) and a block of query tokens.  Each wave owns one differential pair
-// p of that group and 16 query tokens: its 32 query rows (16 tokens x the pair's
-// two heads) are the 32 columns of one MFMA tile, column n = 16*head + token, so
-// the lambda-subtract pairs lanes l and l^16 in registers.  Every K/V tile of 64
+// p of that group and 16 query tokens; the pair's two heads are two 16-column
+// MFMA tiles of the same tokens, so head 0 and head 1 of a token sit in the same
+// lane and the lambda-subtract needs no lane exchange.  Every K/V tile of 64
 // keys is copied from HBM/L2 into LDS once per workgroup and read by all waves:
 // with G = 4 pairs per KV head, one staged byte serves all 8 query heads.  The
 // copy uses the direct global-to-LDS loads (16 bytes per lane, no registers),
 // issued three tiles ahead into a 4-deep ring.  The two waves of a SIMD
 // interleave: one wave's softmax (VALU) issues while the other's MFMAs run.
 //
-// Per 32-key half tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
-// (A = K from LDS, B = Q^T held in registers), so each lane holds the scores of
-// one query row against 16 keys; lane l^32 holds the other 16.  P = exp2(S *
-// log2(e)/sqrt(d) - m) is rounded to bf16 and fed straight from registers as the
-// B operand of O^T += V^T P^T; the V^T operand comes from the row-major V tile
-// via the transposing LDS read.  The running maximum m is raised only when a
-// half tile's row sums could overflow (see the softmax step below).  The
-// epilogue normalises each row, subtracts lambda * head 1 from head 0 of the
-// same token, applies the optional V1 RMSNorm and stores bf16.
+// Per 32-key half tile a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
+// as four independent 16 x 16 tiles (2 key tiles x 2 heads, each summed over D/32
+// k-steps), so no product waits on the one before it; lane l then holds, for
+// each head, the scores of query token l%16 against 8 of the 32 keys.  P =
+// exp2(S * log2(e)/sqrt(d) - m) is rounded to bf16 and fed straight from
+// registers as the B operand of O^T += V^T P^T (16 x 16 tiles, one product per
+// d-tile and head); the V^T operand comes from the row-major V tile via the
+// transposing LDS read, its k order matching the keys each lane holds.  The
+// running maximum m is raised only when a half tile's row sums could overflow
+// (see the softmax step below).  The epilogue normalises each row, subtracts
+// lambda * head 1 from head 0 of the same token, applies the optional V1
+// RMSNorm and stores bf16.
 #include <type_traits>
 
 #include "dev_common.h"
@@ -85,13 +88,6 @@ __device__ __forceinline__ int v_phys(int row, int col) {
   return row * D + ((((col >> 3) ^ v_swz<D>(row))) << 3) + (col & 7);
 }
 
-__device__ __forceinline__ float max16(const f32x16& x) {
-  float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
-#pragma unroll
-  for (int i = 3; i < 15; i += 2) m = fmaxf(fmaxf(m, x[i]), x[i + 1]);
-  return fmaxf(m, x[15]);
-}
-
 template <int D, int SHAPE>
 __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) void prefill_kernel(Args a) {
   constexpr int WAVES = Shape<SHAPE>::WAVES;
@@ -99,8 +95,8 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
   constexpr int BN = Shape<SHAPE>::BN;
   constexpr int HPT = BN / 32;             // 32-key half tiles per tile
   constexpr int NCH = D / 8;               // 16-byte chunks per row
-  constexpr int KSTEPS = D / 16;           // QK^T k-steps
-  constexpr int DBLK = D / 32;             // PV output d-blocks
+  constexpr int KS = D / 32;               // QK^T k-steps (32 d each)
+  constexpr int DT = D / 16;               // PV output d-tiles
   constexpr int LOADS = BN * NCH / THREADS;  // 16-byte chunks per thread per tile (K or V)
   static_assert(LOADS >= 1 && (BN * NCH) % THREADS == 0, "tile/thread mismatch");
   // K/V tiles in a ring: tile t lives in buffer t % NBUF and is requested
@@ -117,8 +113,8 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
   // wave index as a scalar, so everything derived from it (pair, first token,
   // masking decisions) stays wave-uniform and compiles to scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool lo = lane < 32;
-  const int l32 = lane & 31;   // MFMA column: query row 16*head + token
+  const int i16 = lane & 15;   // MFMA column: query token i0 + i16 (both heads)
+  const int g16 = lane >> 4;   // 16-lane group: which keys / d values of a tile
 
   // ---- workgroup -> (token block, b, g, pair chunk).  Token blocks run longest
   // first (causal work grows with the block index); when the (b, g, chunk) units
@@ -149,8 +145,7 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
   const int p = g * a.G + pig;
   const int i0 = tok0 + sub * QT;          // first query token of this wave
   const int T = a.T;
-  const int qtok = i0 + (l32 & 15);        // this lane's query token
-  const int qhead = l32 >> 4;              // 0: positive branch, 1: subtracted branch
+  const int qtok = i0 + i16;               // this lane's query token
 
   // key tiles [t_first, t_first + nt): with a sliding window the tiles that end
   // before the window of the block's first token are never copied or read
@@ -160,23 +155,26 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
   const bf16* kbase = a.k + ((size_t)b * T * a.Hkv + g) * D;
   const bf16* vbase = a.v + ((size_t)b * T * a.Hkv + g) * D;
 
-  // ---- Q^T operand in registers: lane -> query row l32, d = 16*s + 8*(lane/32) + 0..7
-  bf16x8 qreg[KSTEPS];
+  // ---- Q^T operands in registers: head h, k-step s -> lane holds token qtok,
+  // d = 32*s + 8*g16 + 0..7 (the B layout of the 16x16x32 product)
+  bf16x8 qreg[2][KS];
   {
     const bool ok = active && qtok < T;
-    const bf16* src = a.q + (((size_t)b * T + (ok ? qtok : 0)) * a.Hq + 2 * p + qhead) * D + 8 * (lane >> 5);
+    const bf16* src = a.q + (((size_t)b * T + (ok ? qtok : 0)) * a.Hq + 2 * p) * D + 8 * g16;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      u32x4 x = ok ? ldg16(src + 16 * s) : u32x4{0, 0, 0, 0};
-      qreg[s] = __builtin_bit_cast(bf16x8, x);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4 x = ok ? ldg16(src + h * D + 32 * s) : u32x4{0, 0, 0, 0};
+        qreg[h][s] = __builtin_bit_cast(bf16x8, x);
+      }
   }
 
-  f32x16 o[DBLK];
+  f32x4 o[DT][2];   // O^T tiles [d-tile][head]: lane holds d = 16*dt + 4*g16 + 0..3 of token qtok
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
-  float m = -INFINITY;   // running maximum (log2 domain), uniform over lanes l, l^32
-  float l = 0.f;         // this lane's share of the softmax denominator
+  for (int i = 0; i < DT; ++i) o[i][0] = o[i][1] = f32x4{};
+  float m[2] = {-INFINITY, -INFINITY};   // running maxima per head (log2 domain), uniform over the row's 4 lanes
+  float l[2] = {0.f, 0.f};               // this lane's share of each head's softmax denominator
   const float c = a.scale_log2;
 
   // ---- direct global -> LDS tile copy.  Wave-instruction j of wave w fills the
@@ -216,32 +214,32 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
   };
 
   // ---- per-lane LDS read offsets (bytes), loop-invariant
-  const int i16 = lane & 15, g16 = lane >> 4;
-  uint32_t kofs[KSTEPS];   // K rows as the A operand of S^T: row l32, k-step s
+  uint32_t kofs[2][KS];   // K rows as the A operand of S^T: key tile kt (row 16*kt + i16), k-step s
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-    kofs[s] = l32 * D * 2 + 16 * ((2 * s + (lane >> 5)) ^ (l32 & (NCH - 1)));
-  uint32_t vofs[DBLK];     // transposing reads of V for output d-block db
-  {
-    const int vrow = 4 * (g16 >> 1) + (i16 >> 2);
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-      vofs[db] = NBUF * TILE_BYTES + 2 * v_phys<D>(vrow, col);
+    for (int s = 0; s < KS; ++s) {
+      const int r = 16 * kt + i16;
+      kofs[kt][s] = r * D * 2 + 16 * ((4 * s + g16) ^ (r & (NCH - 1)));
     }
-  }
-  // (v_phys of row vrow + 16*ks + 8*r + 32*kb equals v_phys(vrow) + that many rows:
-  // the V swizzle depends on row % 4 only.)
+  // V^T operand of d-tile dt: the lane's 8 k slots are keys 4*g16 + 0..3 and
+  // 16 + 4*g16 + 0..3 (the keys its scores cover), read as two transposing
+  // reads of 4 rows; lane s of a 16-lane group addresses row 4*g16 + s/4,
+  // columns 16*dt + 4*(s%4) .. +3
+  uint32_t vofs[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) vofs[dt] = NBUF * TILE_BYTES + 2 * v_phys<D>(4 * g16 + (i16 >> 2), 16 * dt + 4 * (i16 & 3));
+  // (v_phys of row r + 16 equals v_phys(r) + 16 rows: the V swizzle depends on
+  // row % 4 only.)
 
-  // P = exp2(S*c - mb) as the bf16 B operand, and this lane's share of its row sum
-  auto exp_rows = [&](const f32x16& sh, float mb, bf16x8 (&ph)[2], float& lt) {
+  // P = exp2(S*c - m) of head h as the bf16 B operand (k slot e <-> key tile e/4,
+  // row 4*g16 + e%4), and this lane's share of its row sum
+  auto exp_rows = [&](const f32x4 (&st)[2][2], int h, float mb, bf16x8& ph, float& lt) {
     lt = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ph[i >> 3][i & 7] = (bf16)fast_exp2(__builtin_fmaf(sh[i], c, -mb));
+    for (int e = 0; e < 8; ++e) ph[e] = (bf16)fast_exp2(__builtin_fmaf(st[e >> 2][h][e & 3], c, -mb));
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) lt = dot2_ones(bf16x2{ph[ks][j], ph[ks][j + 1]}, lt);
+    for (int j = 0; j < 8; j += 2) lt = dot2_ones(bf16x2{ph[j], ph[j + 1]}, lt);
   };
 
   // Last 32-key half tile this wave reads; K operands are read one half tile
@@ -249,10 +247,12 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
   const int hl = active ? ((a.causal ? min(T, i0 + QT) : T) + 31) / 32 - 1 : -1;
   // first half tile this wave reads (the window of its first token)
   const int h_first = a.window > 0 ? max(0, i0 - a.window + 1) / 32 : 0;
-  bf16x8 ka[KSTEPS];
+  bf16x8 ka[2][KS];
   auto load_k = [&](int off) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) ka[s] = *reinterpret_cast<const bf16x8*>(lds + kofs[s] + off);
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) ka[kt][s] = *reinterpret_cast<const bf16x8*>(lds + kofs[kt][s] + off);
   };
 
   // half tile h = HPT t + KB, held in ring buffer BUF
@@ -267,61 +267,74 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
     const int kbase_tok = 32 * h;
 
     // ---- V^T operands of this half tile
-    bf16x8 va[2][DBLK];
+    bf16x8 va[DT];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const char* vp = lds + vofs[db] + BUF * TILE_BYTES + (KB * 32 + 16 * ks) * D * 2;
-        va[ks][db] = concat(lds_read_tr4(reinterpret_cast<const bf16*>(vp)),
-                            lds_read_tr4(reinterpret_cast<const bf16*>(vp + 8 * D * 2)));
-      }
-    // ---- S^T = K Q^T (keys x query rows)
+    for (int dt = 0; dt < DT; ++dt) {
+      const char* vp = lds + vofs[dt] + BUF * TILE_BYTES + KB * 32 * D * 2;
+      va[dt] = concat(lds_read_tr4(reinterpret_cast<const bf16*>(vp)),
+                      lds_read_tr4(reinterpret_cast<const bf16*>(vp + 16 * D * 2)));
+    }
+    // ---- S^T = K Q^T: tiles [key tile kt][head], lane -> keys 16*kt + 4*g16 + i
     // raised issue priority while the S products issue: the other wave of the
     // SIMD then tends to run its softmax meanwhile instead of interleaving MFMAs
-    f32x16 sc = f32x16{};
+    f32x4 st[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) st[kt][0] = st[kt][1] = f32x4{};
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) sc = mfma32(ka[s], qreg[s], sc);
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) st[kt][hh] = mfma16(ka[kt][s], qreg[hh][s], st[kt][hh]);
     __builtin_amdgcn_s_setprio(0);
     load_k(KNEXT);   // after the last half tile this reads unused (in-bounds) data
     const bool need_mask = (a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T ||
                            (a.window > 0 && kbase_tok + a.window <= i0 + QT - 1);
     if (need_mask) {   // causal diagonal, sequence tail, window start
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const bool vis = key < T && (!a.causal || key <= qtok) && (a.window == 0 || key > qtok - a.window);
-        if (!vis) sc[i] = -INFINITY;
-      }
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase_tok + 16 * kt + 4 * g16 + i;
+          const bool vis = key < T && (!a.causal || key <= qtok) && (a.window == 0 || key > qtok - a.window);
+          if (!vis) st[kt][0][i] = st[kt][1][i] = -INFINITY;
+        }
     }
     // ---- online softmax.  P = exp2(S*c - m) uses the current running maximum
-    // m as is; the half tile's row sums bound every P value (a lane's 16 values
-    // are non-negative), so if all sums stay <= 2^16 nothing overflows and m
-    // needs no update.  Otherwise (and on the first half tile, where m = -inf
-    // makes the sums infinite) a rare branch raises m to the true maximum,
-    // rescales O and l, and recomputes P.  Either way numerator and denominator
-    // share one reference, so the result is exact.
+    // m as is; the half tile's row sums bound every P value (a lane's 8 values
+    // of a row are non-negative), so if all sums stay <= 2^16 nothing overflows
+    // and m needs no update.  Otherwise (and on the first half tile, where m =
+    // -inf makes the sums infinite) a rare branch raises m to the true maximum
+    // (over the row's 4 lanes), rescales O and l, and recomputes P.  Either way
+    // numerator and denominator share one reference, so the result is exact.
     bf16x8 pp[2];
-    float lt;
-    exp_rows(sc, m, pp, lt);
-    if (__builtin_amdgcn_ballot_w64(!(lt <= SUM_LIMIT))) {
-      float mx = max16(sc);
-      mx = fmaxf(mx, partner32(mx, lo)) * c;
-      const float nm = fmaxf(m, mx);
-      const float alpha = (nm == -INFINITY) ? 1.f : fast_exp2(m - nm);
+    float lt[2];
+    exp_rows(st, 0, m[0], pp[0], lt[0]);
+    exp_rows(st, 1, m[1], pp[1], lt[1]);
+    if (__builtin_amdgcn_ballot_w64(!(lt[0] <= SUM_LIMIT) || !(lt[1] <= SUM_LIMIT))) {
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
-      l *= alpha;
-      m = nm;
-      exp_rows(sc, nm == -INFINITY ? 0.f : nm, pp, lt);
+      for (int hh = 0; hh < 2; ++hh) {
+        float mx = fmaxf(fmaxf(fmaxf(st[0][hh][0], st[0][hh][1]), fmaxf(st[0][hh][2], st[0][hh][3])),
+                         fmaxf(fmaxf(st[1][hh][0], st[1][hh][1]), fmaxf(st[1][hh][2], st[1][hh][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+        const float nm = fmaxf(m[hh], mx);
+        const float alpha = (nm == -INFINITY) ? 1.f : fast_exp2(m[hh] - nm);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][hh] *= alpha;
+        l[hh] *= alpha;
+        m[hh] = nm;
+        exp_rows(st, hh, nm == -INFINITY ? 0.f : nm, pp[hh], lt[hh]);
+      }
     }
-    l += lt;
+    l[0] += lt[0];
+    l[1] += lt[1];
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) o[db] = mfma32(va[ks][db], pp[ks], o[db]);
+      for (int hh = 0; hh < 2; ++hh) o[dt][hh] = mfma16(va[dt], pp[hh], o[dt][hh]);
   };
 
   // ---- tile loop, unrolled by NBUF so each buffer index is a constant.
@@ -365,53 +378,60 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
   }
 
   if (!active) return;
-  // ---- epilogue: normalise each row, subtract lambda * head 1 (columns 16-31,
-  // lanes l^16) from head 0 (columns 0-15), optional RMSNorm, store head-0 lanes
-  l += partner32(l, lo);
-  if (a.lse != nullptr && lo && qtok < T)   // natural-log LSE of the row's scaled scores
-    a.lse[((size_t)b * T + qtok) * a.Hq + 2 * p + qhead] = (m + __log2f(l)) * 0.6931471805599453f;
-  const bool ok = qhead == 0 && qtok < T;
+  // ---- epilogue: each row's denominator is spread over the 4 lanes of its
+  // token (g16 = 0..3); normalise, subtract lambda * head 1 from head 0 in the
+  // lane, optional RMSNorm, store
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    l[hh] += __shfl_xor(l[hh], 16);
+    l[hh] += __shfl_xor(l[hh], 32);
+  }
+  const bool ok = qtok < T;
+  if (a.lse != nullptr && g16 == 0 && ok) {   // natural-log LSE of each head's scaled scores
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      a.lse[((size_t)b * T + qtok) * a.Hq + 2 * p + hh] = (m[hh] + __log2f(l[hh])) * 0.6931471805599453f;
+  }
   const float lamv = ok ? a.lam[((size_t)b * T + qtok) * a.P + p] : 0.f;
-  const float inv = 1.0f / l;
+  const float inv0 = 1.0f / l[0], inv1 = 1.0f / l[1];
   float ss = 0.f;
   {
     // Both products are rounded before the subtraction (FMA contraction off), so
     // the two branches are treated alike and identical branches with lambda = 1
-    // cancel exactly.  Head-1 lanes keep their own normalised row (A_2 V).
+    // cancel exactly.  o[.][1] keeps the normalised head-1 row (A_2 V).
 #pragma clang fp contract(off)
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float y = o[db][i] * inv;
-        const float y1 = __shfl_xor(y, 16);
-        const float x = qhead == 0 ? y - lamv * y1 : y;
-        o[db][i] = x;
+      for (int i = 0; i < 4; ++i) {
+        const float y0 = o[dt][0][i] * inv0;
+        const float y1 = o[dt][1][i] * inv1;
+        const float x = y0 - lamv * y1;
+        o[dt][0][i] = x;
+        o[dt][1][i] = y1;
         ss += x * x;
       }
     }
   }
-  auto store_rows = [&](bf16* base) {
-    bf16* dst = base + (((size_t)b * T + qtok) * a.P + p) * D + 4 * (lane >> 5);
+  auto store_rows = [&](bf16* base, int hh) {
+    bf16* dst = base + (((size_t)b * T + qtok) * a.P + p) * D + 4 * g16;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
+    for (int dt = 0; dt < DT; ++dt) {
+      bf16x4 w;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)o[db][4 * i4 + e];
-        *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * i4) = w;
-      }
+      for (int e = 0; e < 4; ++e) w[e] = (bf16)o[dt][hh][e];
+      *reinterpret_cast<bf16x4*>(dst + 16 * dt) = w;
     }
   };
-  if (a.o2 != nullptr && qhead == 1 && qtok < T) store_rows(a.o2);
+  if (a.o2 != nullptr && ok) store_rows(a.o2, 1);
   if (a.v1) {
-    ss += partner32(ss, lo);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
     const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) o[db] *= r;
+    for (int dt = 0; dt < DT; ++dt) o[dt][0] *= r;
   }
-  if (ok) store_rows(a.out);
+  if (ok) store_rows(a.out, 0);
 }
 
 template <int D, int SHAPE>
