@@ -31,9 +31,10 @@
 //              ahead.  Results are added to fp32 accumulators (the query chunks
 //              of one key block run in different workgroups).
 //   bwd_dq:    query-block outer, the forward's structure: 8 waves, each one
-//              pair x 16 tokens (its 32 rows are the MFMA columns), K/V tiles
+//              pair x 16 tokens (one 16-column MFMA tile per head), K/V tiles
 //              streamed through a 4-deep LDS ring shared by the whole group.
-//              Per 32-key half tile: S^T = K Q^T, dP^T = V dout^T, dS^T in
+//              Per 32-key half tile, in 16x16x32 tiles: S^T = K Q^T per head,
+//              dP^T = V dout^T once for both heads (they share dout), dS^T in
 //              registers, dQ^T += K^T dS^T with K^T from the transposing read.
 //   convert:   fp32 dK/dV accumulators -> bf16.
 #include <type_traits>
@@ -476,8 +477,8 @@ constexpr int B_THREADS = 64 * B_WAVES;
 template <int D>
 __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
   constexpr int NCH = D / 8;
-  constexpr int KSTEPS = D / 16;
-  constexpr int DBLK = D / 32;
+  constexpr int KS = D / 32;    // k-steps of the score products (32 d each)
+  constexpr int DT = D / 16;    // 16-wide d tiles of dQ
   constexpr int LOADS = B_BN * NCH / B_THREADS;
   static_assert(LOADS >= 1 && (B_BN * NCH) % B_THREADS == 0, "tile/thread mismatch");
   constexpr int NBUF = 4;
@@ -488,8 +489,8 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool lo = lane < 32;
-  const int l32 = lane & 31;   // MFMA column: query row 16*head + token
+  const int i16 = lane & 15;   // MFMA column: query token i0 + i16 (both heads)
+  const int g16 = lane >> 4;   // 16-lane group: which keys / d values of a tile
 
   // ---- workgroup -> (token block, b, g, pair chunk): the forward's order
   int tb, u;
@@ -517,37 +518,41 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
   const int i0 = tok0 + sub * B_QT;
   const int T = a.T;
   const bool active = sub < a.nsub && pig < a.G && i0 < T;
-  const int qtok = i0 + (l32 & 15);
-  const int qhead = l32 >> 4;
+  const int qtok = i0 + i16;
 
   const int kv_end = a.causal ? min(T, tok0 + tokens_wg) : T;
   const int ntiles = (kv_end + B_BN - 1) / B_BN;
   const bf16* kbase = a.k + ((size_t)b * T * a.Hkv + g) * D;
   const bf16* vbase = a.v + ((size_t)b * T * a.Hkv + g) * D;
 
-  // ---- B operands in registers: Q^T of this lane's row, dout^T of its token
-  bf16x8 qreg[KSTEPS], oreg[KSTEPS];
-  float L2 = 0.f, Dr = 0.f, sr = 0.f;
+  // ---- B operands in registers: Q^T of both heads and dout^T of this lane's
+  // token, d = 32*s + 8*g16 + 0..7; row statistics of both heads
+  bf16x8 qreg[2][KS], oreg[KS];
+  float L2[2] = {0.f, 0.f}, Dr[2] = {0.f, 0.f}, sr[2] = {1.f, 0.f};
   {
     const bool ok = active && qtok < T;
     const int tq = ok ? qtok : 0;
-    const bf16* qs = a.q + (((size_t)b * T + tq) * a.Hq + 2 * p + qhead) * D + 8 * (lane >> 5);
-    const bf16* os = a.dout + (((size_t)b * T + tq) * a.P + p) * D + 8 * (lane >> 5);
+    const bf16* qs = a.q + (((size_t)b * T + tq) * a.Hq + 2 * p) * D + 8 * g16;
+    const bf16* os = a.dout + (((size_t)b * T + tq) * a.P + p) * D + 8 * g16;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      qreg[s] = __builtin_bit_cast(bf16x8, ok ? ldg16(qs + 16 * s) : u32x4{0, 0, 0, 0});
-      oreg[s] = __builtin_bit_cast(bf16x8, ok ? ldg16(os + 16 * s) : u32x4{0, 0, 0, 0});
+    for (int s = 0; s < KS; ++s) {
+      qreg[0][s] = __builtin_bit_cast(bf16x8, ok ? ldg16(qs + 32 * s) : u32x4{0, 0, 0, 0});
+      qreg[1][s] = __builtin_bit_cast(bf16x8, ok ? ldg16(qs + D + 32 * s) : u32x4{0, 0, 0, 0});
+      oreg[s] = __builtin_bit_cast(bf16x8, ok ? ldg16(os + 32 * s) : u32x4{0, 0, 0, 0});
     }
     if (ok) {
       const float* r = a.rs + ((size_t)b * a.P + p) * NF * a.Tpad + tq;
-      L2 = r[(size_t)qhead * a.Tpad];
-      Dr = r[(size_t)(2 + qhead) * a.Tpad];
-      sr = qhead == 0 ? 1.f : -r[(size_t)4 * a.Tpad];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        L2[h] = r[(size_t)h * a.Tpad];
+        Dr[h] = r[(size_t)(2 + h) * a.Tpad];
+      }
+      sr[1] = -r[(size_t)4 * a.Tpad];
     }
   }
-  f32x16 o[DBLK];
+  f32x4 o[DT][2];   // dQ^T tiles [d-tile][head]: lane holds d = 16*dt + 4*g16 + 0..3 of token qtok
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
+  for (int i = 0; i < DT; ++i) o[i][0] = o[i][1] = f32x4{};
   const float c = a.scale_log2;
 
   // ---- direct global -> LDS copies of K and V tiles (same swizzle for both)
@@ -577,17 +582,17 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
   };
 
   // ---- per-lane LDS read offsets
-  uint32_t aofs[KSTEPS];   // K (or V) rows as the A operand: row l32, k-step s
+  uint32_t aofs[2][KS];   // K (or V) rows as the A operand: key tile kt (row 16*kt + i16), k-step s
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) aofs[s] = 2 * t_phys<D>(l32, 16 * s + 8 * (lane >> 5));
-  const int i16 = lane & 15, g16 = lane >> 4;
-  const int rr = 4 * (g16 >> 1) + (i16 >> 2);
-  uint32_t tofs[DBLK][2];  // transposing reads of K for d block db, rows +0 / +8
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db)
+    for (int s = 0; s < KS; ++s) aofs[kt][s] = 2 * t_phys<D>(16 * kt + i16, 32 * s + 8 * g16);
+  // K^T of d-tile dt: the lane's 8 k slots are keys 4*g16 + 0..3 and 16 + 4*g16 +
+  // 0..3 (the keys its dS values cover); lane s of a 16-lane group addresses row
+  // 4*g16 + s/4, columns 16*dt + 4*(s%4) .. +3 (rows 16 apart share the swizzle)
+  uint32_t tofs[DT];
 #pragma unroll
-    for (int h8 = 0; h8 < 2; ++h8)
-      tofs[db][h8] = 2 * t_phys<D>(rr + 8 * h8, 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3));
+  for (int dt = 0; dt < DT; ++dt) tofs[dt] = 2 * t_phys<D>(4 * g16 + (i16 >> 2), 16 * dt + 4 * (i16 & 3));
 
   auto compute_tile = [&](int t, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
@@ -599,56 +604,70 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
       constexpr int KO = BUF * TILE_BYTES;
       constexpr int VO = (NBUF + BUF) * TILE_BYTES;
       const int ro = kb * 32 * D * 2;
-      // S^T = K Q^T and dP^T = V dout^T (keys x rows)
-      f32x16 st = f32x16{}, dpt = f32x16{};
-      bf16x8 kva[2][2];
-      auto load_kv = [&](int s, bf16x8 (&o)[2]) {
-        o[0] = *reinterpret_cast<const bf16x8*>(lds + KO + ro + aofs[s]);
-        o[1] = *reinterpret_cast<const bf16x8*>(lds + VO + ro + aofs[s]);
+      // S^T = K Q^T per head and dP^T = V dout^T (keys x tokens); lane -> keys
+      // 16*kt + 4*g16 + i of token qtok.  K/V operands read one k-step ahead.
+      f32x4 st[2][2], dpt[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) st[kt][0] = st[kt][1] = dpt[kt] = f32x4{};
+      bf16x8 kva[2][2][2];   // [buffer][key tile][K, V]
+      auto load_kv = [&](int s, bf16x8 (&ov)[2][2]) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          ov[kt][0] = *reinterpret_cast<const bf16x8*>(lds + KO + ro + aofs[kt][s]);
+          ov[kt][1] = *reinterpret_cast<const bf16x8*>(lds + VO + ro + aofs[kt][s]);
+        }
       };
       load_kv(0, kva[0]);
       // raised issue priority while these products issue, as in the forward: the
       // other wave of the SIMD then tends to run its dS and dQ work meanwhile
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        if (s + 1 < KSTEPS) load_kv(s + 1, kva[(s + 1) & 1]);
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) load_kv(s + 1, kva[(s + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        st = mfma32(kva[s & 1][0], qreg[s], st);
-        dpt = mfma32(kva[s & 1][1], oreg[s], dpt);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          st[kt][0] = mfma16(kva[s & 1][kt][0], qreg[0][s], st[kt][0]);
+          st[kt][1] = mfma16(kva[s & 1][kt][0], qreg[1][s], st[kt][1]);
+          dpt[kt] = mfma16(kva[s & 1][kt][1], oreg[s], dpt[kt]);
+        }
       }
       __builtin_amdgcn_s_setprio(0);
       // hidden keys (future, or past T) get score -inf: P and dS come out 0
       if ((a.causal && kbase_tok + 31 > i0) || kbase_tok + 32 > T) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase_tok + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          const bool vis = key < T && (!a.causal || key <= qtok);
-          st[i] = vis ? st[i] : -INFINITY;
-        }
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase_tok + 16 * kt + 4 * g16 + i;
+            const bool vis = key < T && (!a.causal || key <= qtok);
+            st[kt][0][i] = vis ? st[kt][0][i] : -INFINITY;
+            st[kt][1][i] = vis ? st[kt][1][i] : -INFINITY;
+          }
       }
+      // dS^T of head h as the bf16 B operand: k slot e <-> key tile e/4, row 4*g16 + e%4
       bf16x8 ds[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(__builtin_fmaf(st[i], c, -L2));
-        ds[i >> 3][i & 7] = (bf16)(pv * __builtin_fmaf(sr, dpt[i], -Dr));
-      }
-      // dQ^T += K^T dS^T (K^T operands read one product ahead)
-      constexpr int NIT = 2 * DBLK;
-      auto load_kt = [&](int it) {
-        const int ks = it / DBLK, db = it % DBLK;
-        const char* p0 = lds + KO + ro + 16 * ks * D * 2 + tofs[db][0];
-        const char* p1 = lds + KO + ro + 16 * ks * D * 2 + tofs[db][1];
-        return concat(lds_read_tr4(reinterpret_cast<const bf16*>(p0)),
-                      lds_read_tr4(reinterpret_cast<const bf16*>(p1)));
-      };
-      bf16x8 kt[2];
-      kt[0] = load_kt(0);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        if (it + 1 < NIT) kt[(it + 1) & 1] = load_kt(it + 1);
+        for (int e = 0; e < 8; ++e) {
+          const float pv = fast_exp2(__builtin_fmaf(st[e >> 2][h][e & 3], c, -L2[h]));
+          ds[h][e] = (bf16)(pv * __builtin_fmaf(sr[h], dpt[e >> 2][e & 3], -Dr[h]));
+        }
+      // dQ^T += K^T dS^T (K^T operands read one d-tile ahead; each feeds both heads)
+      auto load_kt = [&](int dt) {
+        const char* p0 = lds + KO + ro + tofs[dt];
+        return concat(lds_read_tr4(reinterpret_cast<const bf16*>(p0)),
+                      lds_read_tr4(reinterpret_cast<const bf16*>(p0 + 16 * D * 2)));
+      };
+      bf16x8 ktr[2];
+      ktr[0] = load_kt(0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        if (dt + 1 < DT) ktr[(dt + 1) & 1] = load_kt(dt + 1);
         __builtin_amdgcn_sched_barrier(0);
-        o[it % DBLK] = mfma32(kt[it & 1], ds[it / DBLK], o[it % DBLK]);
+        o[dt][0] = mfma16(ktr[dt & 1], ds[0], o[dt][0]);
+        o[dt][1] = mfma16(ktr[dt & 1], ds[1], o[dt][1]);
       }
     }
   };
@@ -678,17 +697,16 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
   }
 
   if (!active || qtok >= T) return;
-  // C layout of dQ^T: lane = row (head qhead, token qtok), register i ->
-  // d = 32 db + 8 (i/4) + 4 (lane/32) + i%4
-  bf16* dst = a.dq + (((size_t)b * T + qtok) * a.Hq + 2 * p + qhead) * D + 4 * (lane >> 5);
+  // dQ^T tiles: lane -> token qtok, d = 16*dt + 4*g16 + 0..3
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db) {
+  for (int h = 0; h < 2; ++h) {
+    bf16* dst = a.dq + (((size_t)b * T + qtok) * a.Hq + 2 * p + h) * D + 4 * g16;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
+    for (int dt = 0; dt < DT; ++dt) {
       bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[db][4 * i4 + e] * a.rsqrt_d);
-      *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * i4) = w;
+      for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[dt][h][e] * a.rsqrt_d);
+      *reinterpret_cast<bf16x4*>(dst + 16 * dt) = w;
     }
   }
 }
