@@ -73,6 +73,11 @@ def _median(xs):
 # ----------------------------------------------------------------------------
 # the oracle on the host's cores
 # ----------------------------------------------------------------------------
+def progress(section: str) -> None:
+    """One line on stderr per finished section (the JSON result goes to stdout)."""
+    print(f"bench.py: section {section} done", file=sys.stderr, flush=True)
+
+
 def cpu_baseline() -> dict:
     """The fp64 oracle, as it stands, on each workload: in full where it takes
     seconds, otherwise on a labelled sample extrapolated to the whole workload."""
@@ -305,6 +310,8 @@ def main() -> int:
         del P3, D5
         torch.cuda.empty_cache()
 
+    if do["main"]:
+        progress("main")
     # ---- T=4096 prefill and B=64, L=8192 decode -------------------------------------
     if do["short"]:
         P2, D4 = prefill_inputs(w2), decode_inputs(w4)
@@ -323,6 +330,8 @@ def main() -> int:
         del P2, D4
         torch.cuda.empty_cache()
 
+    if do["short"]:
+        progress("short")
     # ---- training forward + backward on the T=4096 prefill ---------------------------
     if do["backward"]:
         P2 = prefill_inputs(w2)
@@ -353,6 +362,8 @@ def main() -> int:
         del P2, bdout, tout, to2, tlse, bws, grads
         torch.cuda.empty_cache()
 
+    if do["backward"]:
+        progress("backward")
     # ---- serving variants -------------------------------------------------------------
     if do["serving"]:
         # the T=4096 prefill with a 1024-key causal window, and the B=64, L=8192 decode
@@ -389,6 +400,8 @@ def main() -> int:
         del P2, D4, lens, vws
         torch.cuda.empty_cache()
 
+    if do["serving"]:
+        progress("serving")
     # ---- decode layouts: standard transformer, DIFF V1, V2 ---------------------------
     if do["layouts"]:
         # the pages' decode-speed claim on the B=64, L=8192 cache geometry (Hkv=8,
@@ -424,6 +437,8 @@ def main() -> int:
         del cq, ck, cv, clam, D4, cws, cout
         torch.cuda.empty_cache()
 
+    if do["layouts"]:
+        progress("layouts")
     # ---- projections either side of the core ------------------------------------------
     if do["projections"]:
         # lambda for 4096 tokens x 32 pairs from d_model = 4096, and O_W from P*d = 4096
@@ -463,6 +478,8 @@ def main() -> int:
         del jx, jw, ja, jo, jl, jy, jy2
         torch.cuda.empty_cache()
 
+    if do["projections"]:
+        progress("projections")
     # ---- signal-plus-noise SNR from the device's outputs --------------------------------
     if do["snr"]:
         res["snr"] = snr_section(W, bd, torch, np, dev, dev_bf16)
@@ -481,6 +498,8 @@ def main() -> int:
                            unit=first["unit"])
                 break
         res.setdefault("ms_per_step", None)
+    if do["snr"]:
+        progress("snr")
     if not args.no_cpu_baseline and do["main"]:
         res["cpu_baseline"] = cpu_baseline()
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
