@@ -50,16 +50,28 @@ constexpr int NF = kBackwardFields;   // row-statistics fields: lse2_1, lse2_2, 
 
 // ---------------------------------------------------------------------------
 // LDS tile layout shared by every tile here: unpadded row-major [row][d], the
-// 16-byte chunks of a row XOR-permuted by swz(row), which swaps the two low bit
-// fields of the row index: ((row % 4) << 2) | (row / 4 % 4) for 16 chunks per row
-// (((row % 4) << 1) | (row / 4 % 2) for 8).  It is a bijection on 16 (8)
-// consecutive rows, so a row read (ds_read_b128 of consecutive rows at one
-// chunk) spreads over all chunks, and for 4 consecutive rows it differs in its
-// upper bits, so a transposing read (4 rows x 2 chunks per 16 lanes) touches 8
-// distinct chunks.  Rows 16 apart share the permutation.
+// 16-byte chunks of a row XOR-permuted by a function of the row so that the MFMA
+// operand reads hit distinct banks (rows 16 apart share the permutation).  The
+// dK/dV kernel's Q / dout tiles use t_swz(row), which swaps the two low bit fields
+// of the row index: ((row % 4) << 2) | (row / 4 % 4) for 16 chunks per row
+// (((row % 4) << 1) | (row / 4 % 2) for 8); its reads (32 consecutive rows at one
+// chunk, and transposing reads of 4 rows x 2 chunks per 16 lanes) are free of bank
+// conflicts.  The dQ kernel's K / V tiles are read by 16x16x32 operand patterns
+// (lanes 16g + i read row i at chunk 4s + g; transposing reads of rows 4g .. 4g + 3
+// at one chunk pair per 16-lane group), which conflict under t_swz; they use
+// q_swz(row) = ((row % 4) << 2) ^ (row / 4 % 2) << 1 ^ 11 (row / 8 % 2) for 16 chunks,
+// chosen by measurement (rocprofv3 SQ_LDS_BANK_CONFLICT on the patterns alone).
 template <int D>
 __device__ __forceinline__ int t_swz(int row) {
   return D >= 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : (((row & 3) << 1) | ((row >> 2) & 1));
+}
+template <int D>
+__device__ __forceinline__ int q_swz(int row) {
+  return D >= 128 ? (((row & 3) << 2) ^ ((row & 4) >> 1) ^ ((row & 8) ? 11 : 0)) : t_swz<D>(row);
+}
+template <int D>
+__device__ __forceinline__ int q_phys(int row, int col) {
+  return row * D + ((((col >> 3) ^ q_swz<D>(row))) << 3) + (col & 7);
 }
 template <int D>
 __device__ __forceinline__ int t_phys(int row, int col) {
@@ -564,7 +576,7 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
     const int slot = (j * B_WAVES + wave) * 64 + lane;
     const int r = slot / NCH, pc = slot % NCH;
     drow[j] = r;
-    dofs[j] = r * row_bytes + 16 * (pc ^ t_swz<D>(r));
+    dofs[j] = r * row_bytes + 16 * (pc ^ q_swz<D>(r));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)LDS_PTR(const char, lds);
   auto dma_tile = [&](int t, int buf) {
@@ -586,13 +598,13 @@ __global__ __launch_bounds__(B_THREADS, 1) void bwd_dq_kernel(GradArgs a) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) aofs[kt][s] = 2 * t_phys<D>(16 * kt + i16, 32 * s + 8 * g16);
+    for (int s = 0; s < KS; ++s) aofs[kt][s] = 2 * q_phys<D>(16 * kt + i16, 32 * s + 8 * g16);
   // K^T of d-tile dt: the lane's 8 k slots are keys 4*g16 + 0..3 and 16 + 4*g16 +
   // 0..3 (the keys its dS values cover); lane s of a 16-lane group addresses row
   // 4*g16 + s/4, columns 16*dt + 4*(s%4) .. +3 (rows 16 apart share the swizzle)
   uint32_t tofs[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) tofs[dt] = 2 * t_phys<D>(4 * g16 + (i16 >> 2), 16 * dt + 4 * (i16 & 3));
+  for (int dt = 0; dt < DT; ++dt) tofs[dt] = 2 * q_phys<D>(4 * g16 + (i16 >> 2), 16 * dt + 4 * (i16 & 3));
 
   auto compute_tile = [&](int t, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;

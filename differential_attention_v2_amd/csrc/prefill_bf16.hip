@@ -76,12 +76,26 @@ struct Args {
   int units;   // B * Hkv * chunks
 };
 
-// LDS layouts: tiles are row-major [key][d] without padding; 16-byte chunks of a
-// row are XOR-permuted so that the MFMA operand reads hit distinct banks (K: chunk
-// ^ (row % chunks per row); V: chunk ^ v_swz(row)).
+// LDS layouts: tiles are row-major [key][d] without padding; the 16-byte chunks
+// of a row are XOR-permuted by a function of the row so that the MFMA operand
+// reads hit distinct banks.  For d = 128 K and V share swz16(row) = ((row % 4) << 2)
+// ^ (row / 4 % 2) << 1 ^ 11 (row / 8 % 2), chosen by measurement (rocprofv3
+// SQ_LDS_BANK_CONFLICT on the two read patterns alone): it leaves both the K
+// operand reads (ds_read_b128; lanes 16g + i read row i at chunk 4s + g) and the
+// transposing V reads (16-lane group g reads rows 4g .. 4g + 3 at one chunk pair)
+// free of bank conflicts, where chunk ^ (row % 16) conflicts on the V reads and
+// chunk ^ 4 (row % 4) on both.  Rows 16 apart share the permutation.  d = 64 keeps
+// K: chunk ^ (row % 8), V: chunk ^ 4 (row % 2).
+__device__ __forceinline__ int swz16(int row) {
+  return ((row & 3) << 2) ^ ((row & 4) >> 1) ^ ((row & 8) ? 11 : 0);
+}
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return (D >= 128) ? swz16(row) : (row & 7);
+}
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
-  return (D >= 128) ? ((row & 3) << 2) : ((row & 1) << 2);
+  return (D >= 128) ? swz16(row) : ((row & 1) << 2);
 }
 template <int D>
 __device__ __forceinline__ int v_phys(int row, int col) {
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
     const int slot = (j * WAVES + wave) * 64 + lane;
     const int r = slot / NCH, pc = slot % NCH;
     drow[j] = r;
-    dofs_k[j] = r * row_bytes + 16 * (pc ^ (r & (NCH - 1)));
+    dofs_k[j] = r * row_bytes + 16 * (pc ^ k_swz<D>(r));
     dofs_v[j] = r * row_bytes + 16 * (pc ^ v_swz<D>(r));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)LDS_PTR(const char, lds);
@@ -220,7 +234,7 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int r = 16 * kt + i16;
-      kofs[kt][s] = r * D * 2 + 16 * ((4 * s + g16) ^ (r & (NCH - 1)));
+      kofs[kt][s] = r * D * 2 + 16 * ((4 * s + g16) ^ k_swz<D>(r));
     }
   // V^T operand of d-tile dt: the lane's 8 k slots are keys 4*g16 + 0..3 and
   // 16 + 4*g16 + 0..3 (the keys its scores cover), read as two transposing
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(Shape<SHAPE>::THREADS, Shape<SHAPE>::WG_PER_CU) voi
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) vofs[dt] = NBUF * TILE_BYTES + 2 * v_phys<D>(4 * g16 + (i16 >> 2), 16 * dt + 4 * (i16 & 3));
   // (v_phys of row r + 16 equals v_phys(r) + 16 rows: the V swizzle depends on
-  // row % 4 only.)
+  // row % 16 only.)
 
   // P = exp2(S*c - m) of head h as the bf16 B operand (k slot e <-> key tile e/4,
   // row 4*g16 + e%4), and this lane's share of its row sum
