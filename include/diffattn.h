@@ -36,7 +36,16 @@
  *     Device pointers must be non-NULL and 16-byte aligned.  A failed kernel
  *     launch returns DIFFATTN_ERR_HIP; faults inside a kernel surface at the
  *     caller's next synchronisation, as with any HIP call.
- *   - Thread safety: the library is stateless; concurrent calls are safe.
+ *   - Thread safety: concurrent calls are safe, with two pieces of device state
+ *     the library keeps: the fixed scratch of diffattn_decode_fwd_noalloc (see
+ *     there), and the work queues of long prefills.  A prefill (plain, V1 mode or
+ *     training forward; not the sliding window) with at least 8 token blocks per
+ *     CU (e.g. T >= 8192 at Hkv = 8, G = 4) runs as one workgroup per CU taking its
+ *     blocks from queues in a static device array of 1024 slots, one slot per call,
+ *     handed out round-robin; the call's last workgroup empties its slot again.
+ *     So at most 1024 such calls may be in flight on one device at once, and two
+ *     instances of one captured graph that contains such a call must not run
+ *     concurrently (they share its slot).
  */
 #ifndef DIFFATTN_H
 #define DIFFATTN_H
