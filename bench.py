@@ -298,7 +298,7 @@ def main() -> int:
         ms_total = t_start.elapsed_time(t_end)
         ms_pre = _median([e[0].elapsed_time(e[1]) for e in evs])
         ms_dec = _median([e[1].elapsed_time(e[2]) for e in evs])
-        roof = prefill_entry(w3, ms_pre, "prefill_kernel<128, 0>", "prefill_long")
+        roof = prefill_entry(w3, ms_pre, "prefill_kernel<128, 0, true> (persistent, per-XCD work queues)", "prefill_long")
         res.update(value=roof["achieved"], unit="TFLOP/s", ms_per_step=ms_total / args.steps)
         res["roofline"] = roof
         res["roofline_decode"] = decode_entry(w5, ms_dec, "decode_long")
@@ -325,7 +325,7 @@ def main() -> int:
 
         settle(lambda: sstep(None), min(args.settle_ms, 100.0))
         ms_p2, ms_d4 = time_parts(sstep, 2, args.steps, max(3, args.warmup))
-        res["short_configs"] = {"prefill": prefill_entry(w2, ms_p2, "prefill_kernel<128, 0>", "prefill"),
+        res["short_configs"] = {"prefill": prefill_entry(w2, ms_p2, "prefill_kernel<128, 0, false>", "prefill"),
                                 "decode": decode_entry(w4, ms_d4, "decode")}
         del P2, D4
         torch.cuda.empty_cache()
@@ -389,7 +389,7 @@ def main() -> int:
         res["serving"] = {
             "prefill_window": {"value": fw / (ms_sw * 1e-3) / 1e12, "unit": "TFLOP/s",
                                "ms_per_launch": ms_sw, "window": SWA, "algorithmic_flops_per_launch": fw,
-                               "kernel": "prefill_kernel<128, 1>", "traffic": _traffic("prefill_window"),
+                               "kernel": "prefill_kernel<128, 1, false>", "traffic": _traffic("prefill_window"),
                                "frac": fw / (ms_sw * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                "workload": f"{w2.name} causal, window {SWA}"},
             "decode_varlen": {"value": vl_bytes / (ms_vl * 1e-3) / 1e9, "unit": "GB/s", "ms_per_launch": ms_vl,
