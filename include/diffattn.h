@@ -24,7 +24,9 @@
  *   - Pointers marked "device" are device memory owned by the caller; the library
  *     never allocates, frees, or keeps them, and never synchronises.  Work is
  *     enqueued on `stream` (a hipStream_t; NULL = the legacy default stream) and
- *     completes asynchronously.  Outputs must not alias inputs.
+ *     completes asynchronously (the backward forks part of it onto a side stream
+ *     of `stream` and joins it back, see Thread safety).  Outputs must not alias
+ *     inputs.
  *   - Element types: dtype DIFFATTN_BF16 (q/k/v/out are bf16, fp32 accumulation)
  *     or DIFFATTN_FP32 (q/k/v/out are fp32).  lambda is always fp32.
  *   - Layouts are row-major with the head dim fastest ("BTHD").
@@ -45,7 +47,13 @@
  *     handed out round-robin; the call's last workgroup empties its slot again.
  *     So at most 1024 such calls may be in flight on one device at once, and two
  *     instances of one captured graph that contains such a call must not run
- *     concurrently (they share its slot).
+ *     concurrently (they share its slot).  The backward also keeps state: it runs
+ *     its row statistics and dQ kernel on a side stream of `stream` (one per
+ *     stream and device, with three events, created on its first call on that
+ *     stream outside graph capture and kept until the process ends), forked off
+ *     and joined back with events, so work enqueued on `stream` after the call
+ *     still sees every output; a capture of `stream` holds the fork and the join
+ *     (a stream whose first backward call is captured runs it serially).
  */
 #ifndef DIFFATTN_H
 #define DIFFATTN_H

@@ -1,6 +1,7 @@
 """Stream and graph semantics of the C ABI (needs an MI355X).
 
-Every entry point enqueues its kernels on the stream it is given, allocates
+Every entry point enqueues its kernels on the stream it is given (the backward
+forks part of them onto a side stream of it and joins them back), allocates
 nothing and never synchronises (include/diffattn.h).  So the same calls
 (1) give bitwise the same results on a side stream as on the default stream, and
 (2) can be captured into a HIP graph and replayed: each replay, with new inputs
@@ -159,3 +160,48 @@ def test_graph_capture_replays_match_eager(gpu_device):
         if prev is not None:
             assert not torch.equal(got["pre"], prev) and not torch.equal(got["var"], prev_var)
         prev, prev_var = got["pre"], got["var"]
+
+
+GRADS = ("dq", "dk", "dv", "dlam")
+
+
+def test_backward_fork_join_inside_capture(gpu_device):
+    """The backward runs its row statistics and dQ kernel on a side stream of the
+    caller's stream, forked off and joined back with events.  On a stream that has
+    run the backward eagerly (its side stream exists), a capture holds the fork and
+    the join: every replay, with new inputs, equals eager calls, and copies of the
+    gradients captured after the call on the same stream see their final values."""
+    x = _to_device(_host_inputs(0), gpu_device)
+    o = _buffers(gpu_device)
+    s = torch.cuda.Stream(device=gpu_device)   # default priority
+    s.wait_stream(torch.cuda.current_stream())
+
+    def step(bufs):
+        out, o2, lse = bd.prefill_train(x["q"], x["k"], x["v"], x["lam"])
+        bd.prefill_backward(x["q"], x["k"], x["v"], x["lam"], out, o2, lse, x["dout"], workspace=bufs["ws_bwd"],
+                            grads=tuple(bufs[n] for n in GRADS))
+        return {n: bufs[n].clone() for n in GRADS}   # enqueued right after the call, no synchronisation
+
+    with torch.cuda.stream(s):
+        step(o)                                     # eager first: creates the side stream of s
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        copies = step(o)
+
+    o_eager = _buffers(gpu_device)
+    for rep in range(1, 4):
+        fresh = _to_device(_host_inputs(rep), gpu_device)
+        for n in x:
+            x[n].copy_(fresh[n])
+        for n in GRADS:
+            copies[n].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {n: copies[n].clone() for n in GRADS}
+        ref = step(o_eager)
+        torch.cuda.synchronize()
+        _compare(got, ref, f"backward replay {rep}")
