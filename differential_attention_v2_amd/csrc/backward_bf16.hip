@@ -740,39 +740,56 @@ struct SideStream {
 };
 std::mutex side_mu;   // guards side_streams and orders the enqueue sequences
 
-// The entry for s on the current device; side stays null if anything could not be
-// created, and nothing is created while s is being captured into a graph (a stream
-// that first meets the backward inside a capture runs it serially there; one that
-// met it before forks and joins inside the capture too).  With a null side all
-// launches go to s, in the same order of dependencies.
+// The entry for s (on the device s belongs to); side stays null if anything could
+// not be created, once kMaxSideStreams caller streams have one, and while s is being
+// captured into a graph (a stream that first meets the backward inside a capture
+// runs it serially there; one that met it before forks and joins inside the capture
+// too).  With a null side all launches go to s, in the same order of dependencies.
+constexpr size_t kMaxSideStreams = 64;
 SideStream& side_for(hipStream_t s) {
   static std::map<std::pair<int, hipStream_t>, SideStream> side_streams;
+  static size_t created = 0;
+  static SideStream none;
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  SideStream& e = side_streams[{dev, s}];
-  if (e.side == nullptr && dev >= 0) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
-      (void)hipGetLastError();
-      cs = hipStreamCaptureStatusActive;
-    }
-    if (cs != hipStreamCaptureStatusNone) return e;
-    SideStream n;
-    bool ok = hipStreamCreateWithFlags(&n.side, hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&n.pre, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&n.join, hipEventDisableTiming) == hipSuccess;
-    if (ok) {
-      e = n;
-    } else {
-      (void)hipGetLastError();   // clear the failed call's sticky status
-      if (n.join) (void)hipEventDestroy(n.join);
-      if (n.pre) (void)hipEventDestroy(n.pre);
-      if (n.fork) (void)hipEventDestroy(n.fork);
-      if (n.side) (void)hipStreamDestroy(n.side);
-    }
+  if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return none;
   }
-  return e;
+  const auto key = std::make_pair(dev, s);
+  auto it = side_streams.find(key);
+  if (it != side_streams.end()) return it->second;
+  if (created >= kMaxSideStreams) return none;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return none;
+  }
+  if (cs != hipStreamCaptureStatusNone) return none;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) {
+    (void)hipGetLastError();
+    return none;
+  }
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) {   // the side stream lives on s's device
+    (void)hipGetLastError();
+    return none;
+  }
+  SideStream n;
+  bool ok = hipStreamCreateWithFlags(&n.side, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&n.pre, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&n.join, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();   // clear the failed call's status
+    if (n.join) (void)hipEventDestroy(n.join);
+    if (n.pre) (void)hipEventDestroy(n.pre);
+    if (n.fork) (void)hipEventDestroy(n.fork);
+    if (n.side) (void)hipStreamDestroy(n.side);
+  }
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (!ok) return none;
+  ++created;
+  return side_streams.emplace(key, n).first->second;
 }
 
 template <int D>

@@ -49,11 +49,12 @@
  *     instances of one captured graph that contains such a call must not run
  *     concurrently (they share its slot).  The backward also keeps state: it runs
  *     its row statistics and dQ kernel on a side stream of `stream` (one per
- *     stream and device, with three events, created on its first call on that
- *     stream outside graph capture and kept until the process ends), forked off
- *     and joined back with events, so work enqueued on `stream` after the call
- *     still sees every output; a capture of `stream` holds the fork and the join
- *     (a stream whose first backward call is captured runs it serially).
+ *     stream, on that stream's device, with three events, created on its first
+ *     call on that stream outside graph capture and kept until the process ends;
+ *     at most 64 of them), forked off and joined back with events, so work
+ *     enqueued on `stream` after the call still sees every output; a capture of
+ *     `stream` holds the fork and the join.  A stream whose first backward call
+ *     is captured, and every stream past the 64th, runs it serially instead.
  */
 #ifndef DIFFATTN_H
 #define DIFFATTN_H
