@@ -205,3 +205,30 @@ def test_backward_fork_join_inside_capture(gpu_device):
         ref = step(o_eager)
         torch.cuda.synchronize()
         _compare(got, ref, f"backward replay {rep}")
+
+
+def test_backward_on_many_streams(gpu_device):
+    """One side stream per caller stream, at most 64: calls on 70 streams (the last
+    ones past the cap run serially) all give the same gradients, each read right
+    after its call on its own stream."""
+    w = W.Workload("many_streams_bwd", "prefill", "bf16", B=1, T=96, Hq=8, Hkv=2, d=64, qkv_scale=1 / np.sqrt(2),
+                   seed=9250)
+    h = W.make_prefill(w)
+    q, k, v = (to_device(h[n], "bf16", gpu_device) for n in ("q", "k", "v"))
+    lam = torch.from_numpy(h["lam"]).to(gpu_device)
+    dout = to_device(W.make_dout(w), "bf16", gpu_device)
+    out, o2, lse = bd.prefill_train(q, k, v, lam)
+    ref = bd.prefill_backward(q, k, v, lam, out, o2, lse, dout)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=gpu_device) for _ in range(70)]
+    got = []
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            g = bd.prefill_backward(q, k, v, lam, out, o2, lse, dout)
+            got.append(tuple(t.clone() for t in g))   # on s, right after the call
+    for s in streams:
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i, g in enumerate(got):
+        _compare(dict(zip(GRADS, g)), dict(zip(GRADS, ref)), f"stream {i}")
