@@ -39,6 +39,7 @@ namespace diffattn {
 namespace {
 
 constexpr int KSTEP = 32;   // keys per step
+constexpr int kPlanHereMaxB = 1024;   // ragged caches: largest batch whose waves plan their own rows
 
 struct Args {
   const bf16* q;
@@ -55,9 +56,11 @@ struct Args {
   int window;            // visible keys before and including the query, 0 = all
   int nq;                // query heads per KV head served by one wave (<= 16)
   int qoff, koff;        // start of the dot-product slice within q and k rows
-  const int* plan;       // ragged caches: row offsets per sequence, total, rows per range
+  int* plan;             // ragged caches: row offsets per sequence, total, rows per range
   int nslot;             // ragged caches: record slots per query head
   int fuse;              // one key range per sequence: the split kernel writes out itself
+  int plan_here;         // ragged caches: each wave derives its rows from seq_lens (the plan
+                         // kernel is skipped; wave 0 of range 0 writes the plan for the combine)
 };
 
 // V rows in LDS: row-major [key][d], 16-byte chunks XOR-permuted per row so the
@@ -348,35 +351,100 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int* seq_lens, 
 // One wave per (range w, KV head g): the rows [w*Kw, (w+1)*Kw) of the batch's
 // concatenated valid rows, one partial record per sequence the range touches,
 // in slot w + b (unique: a later range never reaches back to an earlier sequence).
+// Valid rows of sequence b: its length clamped to [1, L], the last `window` of them
+// with a window.
+__device__ __forceinline__ int valid_rows(const Args& a, int b) {
+  const int Lb = min(a.L, max(1, a.seq_lens[b]));
+  return a.window > 0 ? min(Lb, a.window) : Lb;
+}
+
+// Sum over the wave of v, in every lane.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Inclusive prefix sum over the wave (lane l: v of lanes 0..l).
+__device__ __forceinline__ int wave_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
 template <int D, int DK>
 __global__ __launch_bounds__(64) void decode_flat_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char lds[DecodeLds<D, DK>::BYTES];
   const int g = blockIdx.x % a.Hkv;
   const int w = blockIdx.x / a.Hkv;
-  const int* plan = a.plan;
-  const int total = plan[a.B];
-  const int Kw = plan[a.B + 1];
+  const int lane = threadIdx.x;
+  int* const plan = a.plan;
+  int total, Kw, b, pb;   // rows of the batch, rows per range, first sequence of this range and its first row
+  if (a.plan_here) {
+    // the plan kernel's arithmetic, per wave: total rows, rows per range, and the
+    // sequence holding row w * Kw (wave 0 of range 0 also writes the plan)
+    total = 0;
+    for (int c0 = 0; c0 < a.B; c0 += 64) total += wave_sum(c0 + lane < a.B ? valid_rows(a, c0 + lane) : 0);
+    total = __builtin_amdgcn_readfirstlane(total);
+    const int nw = a.nslot - a.B;
+    const int per = (total + nw - 1) / nw;
+    Kw = max(32, (per + 31) / 32 * 32);
+    const int x0 = w * Kw;
+    const bool writer = w == 0 && g == 0;
+    b = -1;
+    pb = 0;
+    int carry = 0;
+    for (int c0 = 0; c0 < a.B && (b < 0 || writer); c0 += 64) {
+      const bool in = c0 + lane < a.B;
+      const int v = in ? valid_rows(a, c0 + lane) : 0;
+      const int incl = wave_scan(v, lane);
+      if (writer && in) plan[c0 + lane] = carry + incl - v;
+      const unsigned long long hit = __ballot(in && carry + incl > x0);
+      if (b < 0 && hit != 0ull) {   // wave-uniform values, kept in scalar registers
+        const int l = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+        b = c0 + l;
+        pb = __builtin_amdgcn_readfirstlane(carry + __shfl(incl - v, l));
+      }
+      carry = __builtin_amdgcn_readfirstlane(carry + __shfl(incl, 63));
+    }
+    if (writer && lane == 0) {
+      plan[a.B] = total;
+      plan[a.B + 1] = Kw;
+    }
+    if (b < 0) return;   // this range starts past the last row
+  } else {
+    total = plan[a.B];
+    Kw = plan[a.B + 1];
+    const int x0 = w * Kw;
+    if (x0 >= total) return;
+    int lo_b = 0, hi_b = a.B - 1;   // last b with plan[b] <= x0
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (plan[mid] <= x0) lo_b = mid; else hi_b = mid - 1;
+    }
+    b = lo_b;
+    pb = plan[b];
+  }
   int x = w * Kw;
   const int xend = min(total, x + Kw);
   if (x >= xend) return;
-  int lo_b = 0, hi_b = a.B - 1;   // last b with plan[b] <= x
-  while (lo_b < hi_b) {
-    const int mid = (lo_b + hi_b + 1) >> 1;
-    if (plan[mid] <= x) lo_b = mid; else hi_b = mid - 1;
-  }
-  int b = lo_b;
   const int rec = D + 4;
   const size_t hstride = (size_t)a.nslot * rec;
   while (x < xend) {
-    const int seg_end = min(xend, plan[b + 1]);
+    const int n = valid_rows(a, b);            // rows of sequence b: [pb, pb + n) of the batch
+    const int seg_end = min(xend, pb + n);
     if (seg_end > x) {
       const int Lb = min(a.L, max(1, a.seq_lens[b]));
       const int lo = a.window > 0 ? max(0, Lb - a.window) : 0;
-      const int k0 = lo + (x - plan[b]);
+      const int k0 = lo + (x - pb);
       attend_range<D, DK>(a, lds, b, g, k0, k0 + (seg_end - x),
                           a.ws + ((size_t)(g * a.nq) * a.nslot + w + b) * rec, hstride);
       x = seg_end;
     }
+    pb += n;
     ++b;
   }
 }
@@ -574,10 +642,15 @@ hipError_t launch(const DecodeProblem& pr, hipStream_t st) {
   a.plan = nullptr;
   a.nslot = 0;
   a.fuse = 0;
+  a.plan_here = 0;
   if (pr.flat_ranges > 0) {   // ragged caches: even split of the batch's valid rows
     int* plan = reinterpret_cast<int*>(pr.ws + decode_flat_record_floats(pr.B, pr.Hq, pr.d, pr.flat_ranges));
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, pr.seq_lens, pr.B, pr.L, pr.window,
-                       pr.flat_ranges, plan);
+    // up to kPlanHereMaxB sequences every wave scans the lengths itself (a few
+    // loads); beyond, one plan kernel scans them once for all waves
+    a.plan_here = pr.B <= kPlanHereMaxB ? 1 : 0;
+    if (!a.plan_here)
+      hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, st, pr.seq_lens, pr.B, pr.L, pr.window,
+                         pr.flat_ranges, plan);
     a.plan = plan;
     a.nslot = pr.flat_ranges + pr.B;
     hipLaunchKernelGGL((decode_flat_kernel<D, D>), dim3((unsigned)(pr.flat_ranges * a.Hkv)), dim3(64), 0, st, a);

@@ -112,7 +112,8 @@ def test_decode_varlen_full_lengths_equal_plain_decode(gpu_device):
 
 
 def test_decode_varlen_many_short_sequences(gpu_device):
-    """1500 sequences of 1-40 rows: ranges cross many sequences, the plan scans B > 1024."""
+    """1500 sequences of 1-40 rows: ranges cross many sequences (a plan kernel scans
+    the lengths once: B > 1024)."""
     w = _decode_case(1500, 64, 8, 2, 64, seed=8450)
     inp, (q, k, v, lam) = _decode_inputs(w, gpu_device)
     lens_np = np.random.default_rng(8).integers(1, 41, size=1500).astype(np.int32)
@@ -123,6 +124,23 @@ def test_decode_varlen_many_short_sequences(gpu_device):
         sel = np.arange(0, 1500, 37)
         ref = oracle.diffattn_decode(f["q"], f["k"], f["v"], inp["lam"], batches=sel, seq_lens=lens_np)
         assert_parity(got[sel], ref, f"1500 short sequences splits={splits}")
+
+
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_decode_varlen_plan_paths(gpu_device, B):
+    """Up to 1024 sequences every wave scans the lengths itself (16 chunks of 64 at
+    B = 1024); from 1025 on a plan kernel scans them once.  Both against the oracle,
+    with and without a window."""
+    w = _decode_case(B, 48, 8, 2, 64, seed=8460 + B)
+    inp, (q, k, v, lam) = _decode_inputs(w, gpu_device)
+    lens_np = np.random.default_rng(B).integers(1, 49, size=B).astype(np.int32)
+    lens = torch.from_numpy(lens_np).to(gpu_device)
+    f = {n: W.to_f64(inp[n], "bf16") for n in ("q", "k", "v")}
+    sel = np.unique(np.concatenate([np.arange(0, B, 41), [B - 2, B - 1]]))
+    for window in (0, 16):
+        got = from_device(bd.decode_varlen(q, k, v, lam, seq_lens=lens, window=window))
+        ref = oracle.diffattn_decode(f["q"], f["k"], f["v"], inp["lam"], batches=sel, seq_lens=lens_np, window=window)
+        assert_parity(got[sel], ref, f"{B} short sequences window={window}")
 
 
 def test_decode_varlen_clamps_out_of_range_lengths(gpu_device):
