@@ -856,13 +856,16 @@ hipError_t launch(const BackwardProblem& pr, hipStream_t s) {
   };
   if (ss.side) {
     chk(hipEventRecord(ss.fork, s));
-    chk(hipStreamWaitEvent(t, ss.fork, 0));
+    if (e == hipSuccess) chk(hipStreamWaitEvent(t, ss.fork, 0));
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)gpre), dim3(256), 0, t, pa);
-  if (ss.side) chk(hipEventRecord(ss.pre, t));
   hipLaunchKernelGGL(fill_zero_kernel, dim3(2048), dim3(256), 0, s, reinterpret_cast<float4*>(dk_acc), 2 * nkv / 4);
-  if (ss.side) chk(hipStreamWaitEvent(s, ss.pre, 0));
+  if (ss.side) {   // without this dependency the gradient kernels must not be enqueued
+    chk(hipEventRecord(ss.pre, t));
+    if (e == hipSuccess) chk(hipStreamWaitEvent(s, ss.pre, 0));
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)ga), dim3(A_THREADS), 0, s, a);
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gb), dim3(B_THREADS), 0, t, a);
   if (ss.side) chk(hipEventRecord(ss.join, t));
@@ -870,7 +873,7 @@ hipError_t launch(const BackwardProblem& pr, hipStream_t s) {
                      static_cast<bf16x4*>(pr.dk), nkv / 4);
   hipLaunchKernelGGL(convert_kernel, dim3(2048), dim3(256), 0, s, reinterpret_cast<const float4*>(dv_acc),
                      static_cast<bf16x4*>(pr.dv), nkv / 4);
-  if (ss.side) chk(hipStreamWaitEvent(s, ss.join, 0));
+  if (ss.side && e == hipSuccess) chk(hipStreamWaitEvent(s, ss.join, 0));
   chk(hipGetLastError());
   return e;
 }
