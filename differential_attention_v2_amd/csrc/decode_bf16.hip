@@ -39,7 +39,10 @@ namespace diffattn {
 namespace {
 
 constexpr int KSTEP = 32;   // keys per step
-constexpr int kPlanHereMaxB = 1024;   // ragged caches: largest batch whose waves plan their own rows
+// ragged caches: largest batch whose waves plan their own rows (the c4-shaped ragged
+// decode at B = 128-512 ran 0.6-0.9 % faster that way than with the plan kernel, at
+// B = 1024 2 % slower)
+constexpr int kPlanHereMaxB = 512;
 
 struct Args {
   const bf16* q;
@@ -385,9 +388,16 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(Args a) {
   int total, Kw, b, pb;   // rows of the batch, rows per range, first sequence of this range and its first row
   if (a.plan_here) {
     // the plan kernel's arithmetic, per wave: total rows, rows per range, and the
-    // sequence holding row w * Kw (wave 0 of range 0 also writes the plan)
+    // sequence holding row w * Kw (wave 0 of range 0 also writes the plan).  All
+    // lengths are requested at once (one memory round trip), then scanned from registers.
+    constexpr int NCHUNK = kPlanHereMaxB / 64;
+    int v[NCHUNK];
+#pragma unroll
+    for (int j = 0; j < NCHUNK; ++j) v[j] = 64 * j + lane < a.B ? valid_rows(a, 64 * j + lane) : 0;
     total = 0;
-    for (int c0 = 0; c0 < a.B; c0 += 64) total += wave_sum(c0 + lane < a.B ? valid_rows(a, c0 + lane) : 0);
+#pragma unroll
+    for (int j = 0; j < NCHUNK; ++j)
+      if (64 * j < a.B) total += wave_sum(v[j]);
     total = __builtin_amdgcn_readfirstlane(total);
     const int nw = a.nslot - a.B;
     const int per = (total + nw - 1) / nw;
@@ -397,16 +407,18 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(Args a) {
     b = -1;
     pb = 0;
     int carry = 0;
-    for (int c0 = 0; c0 < a.B && (b < 0 || writer); c0 += 64) {
+#pragma unroll
+    for (int j = 0; j < NCHUNK; ++j) {
+      const int c0 = 64 * j;
+      if (c0 >= a.B || (b >= 0 && !writer)) break;
       const bool in = c0 + lane < a.B;
-      const int v = in ? valid_rows(a, c0 + lane) : 0;
-      const int incl = wave_scan(v, lane);
-      if (writer && in) plan[c0 + lane] = carry + incl - v;
+      const int incl = wave_scan(v[j], lane);
+      if (writer && in) plan[c0 + lane] = carry + incl - v[j];
       const unsigned long long hit = __ballot(in && carry + incl > x0);
       if (b < 0 && hit != 0ull) {   // wave-uniform values, kept in scalar registers
         const int l = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
         b = c0 + l;
-        pb = __builtin_amdgcn_readfirstlane(carry + __shfl(incl - v, l));
+        pb = __builtin_amdgcn_readfirstlane(carry + __shfl(incl - v[j], l));
       }
       carry = __builtin_amdgcn_readfirstlane(carry + __shfl(incl, 63));
     }

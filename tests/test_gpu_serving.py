@@ -113,7 +113,7 @@ def test_decode_varlen_full_lengths_equal_plain_decode(gpu_device):
 
 def test_decode_varlen_many_short_sequences(gpu_device):
     """1500 sequences of 1-40 rows: ranges cross many sequences (a plan kernel scans
-    the lengths once: B > 1024)."""
+    the lengths once: B > 512)."""
     w = _decode_case(1500, 64, 8, 2, 64, seed=8450)
     inp, (q, k, v, lam) = _decode_inputs(w, gpu_device)
     lens_np = np.random.default_rng(8).integers(1, 41, size=1500).astype(np.int32)
@@ -126,10 +126,10 @@ def test_decode_varlen_many_short_sequences(gpu_device):
         assert_parity(got[sel], ref, f"1500 short sequences splits={splits}")
 
 
-@pytest.mark.parametrize("B", [1024, 1025])
+@pytest.mark.parametrize("B", [512, 513])
 def test_decode_varlen_plan_paths(gpu_device, B):
-    """Up to 1024 sequences every wave scans the lengths itself (16 chunks of 64 at
-    B = 1024); from 1025 on a plan kernel scans them once.  Both against the oracle,
+    """Up to 512 sequences every wave scans the lengths itself (8 chunks of 64 at
+    B = 512); from 513 on a plan kernel scans them once.  Both against the oracle,
     with and without a window."""
     w = _decode_case(B, 48, 8, 2, 64, seed=8460 + B)
     inp, (q, k, v, lam) = _decode_inputs(w, gpu_device)
