@@ -92,6 +92,8 @@ def test_training_forward_matches_prefill_and_oracle(gpu_device):
     (1, 64, 16, 1, 64, True),      # G = 8
     (1, 1, 8, 2, 128, True),       # a single token
     (1, 33, 8, 2, 64, False),      # one row past a tile
+    (1, 1300, 16, 2, 64, False),   # non-causal over several query chunks, d = 64
+    (2, 700, 24, 4, 128, True),    # G = 3 (a partial pair chunk), two batches
 ])
 def test_backward_small(gpu_device, shape):
     B, T, Hq, Hkv, d, causal = shape
